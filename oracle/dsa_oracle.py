@@ -71,7 +71,7 @@ def pool_keys(k_idx: np.ndarray, pool: int = 4) -> np.ndarray:
     """kpool[p] = mean of token keys 4p..4p+3, for every complete pool."""
     k_idx = np.asarray(k_idx, dtype=np.float64)
     n = k_idx.shape[0] // pool
-    return k_idx[: n * pool].reshape(n, pool, -1).mean(axis=1)
+    return k_idx[: n * pool].reshape(n, pool, k_idx.shape[1]).mean(axis=1)
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,130 @@
+"""C ABI checks that need no GPU: every declared symbol is exported, the
+workspace queries are consistent, and host-side validation rejects bad
+arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_topk_amd as D
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported_and_bound():
+    names = _declared()
+    assert names == sorted(D.SIGNATURES), "binding and header disagree"
+    L = D.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_exported_symbols_are_only_the_abi():
+    out = os.popen(f"nm -D --defined-only {D.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r" T (dsa_[a-z0-9_]+)", out)))
+    assert exported == _declared()
+
+
+def test_status_strings():
+    L = D.lib()
+    assert L.dsa_version() >= 100
+    for s in range(5):
+        assert L.dsa_status_string(s)
+    assert L.dsa_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    a = D.index_topk_ws_bytes(4096, 4096, 128)
+    b = D.index_topk_ws_bytes(1 << 20, 1 << 20, 512)
+    assert 0 < a < b < 2 * 2**30          # chunked indexer scratch stays below 2 GiB
+    assert D.index_topk_ws_bytes(131072, 131072, 128) < 2**30
+    assert D.lib().dsa_index_topk_ws_bytes(10, 10, 4, 64, 4, 0, 1) == 0
+    assert D.sparse_attn_bwd_ws_bytes(10, 1000, 4) >= 2 * 1000 * 128 * 4
+
+
+P = 1 << 20  # a fake, 16-byte aligned address: validation fails before any use
+
+
+def _idx(**kw):
+    a = dict(q_idx=P, k_idx=P, w_idx=P, q_pos=None, Sq=64, Sk=64, heads=4, dim=64, pool=4,
+             topk=8, q_chunk=256, out=P, ws=P, ws_bytes=1 << 40)
+    a.update(kw)
+    return D.lib().dsa_index_topk(a["q_idx"], a["k_idx"], a["w_idx"], a["q_pos"], a["Sq"], a["Sk"],
+                                  a["heads"], a["dim"], a["pool"], a["topk"], a["q_chunk"],
+                                  a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q_idx=None), 1, "q_idx is NULL"),
+    (dict(k_idx=P + 8), 1, "k_idx is not 16-byte aligned"),
+    (dict(out=None), 1, "idx_out is NULL"),
+    (dict(Sq=0), 1, "must be >= 1"),
+    (dict(Sq=65, Sk=64), 1, "Sq=65 > Sk=64"),
+    (dict(q_pos=P + 2), 1, "q_pos is not 4-byte aligned"),
+    (dict(Sk=1 << 31), 2, "< 2^31"),
+    (dict(dim=128), 2, "idx_dim=128"),
+    (dict(heads=5), 2, "idx_heads=5"),
+    (dict(pool=8), 2, "pool=8"),
+    (dict(topk=0), 2, "topk=0"),
+    (dict(topk=4096), 2, "topk=4096"),
+    (dict(q_chunk=0), 1, "q_chunk=0"),
+    (dict(ws_bytes=100), 3, "ws_bytes=100"),
+])
+def test_index_validation(kw, status, msg):
+    assert _idx(**kw) == status
+    assert msg in D.lib().dsa_last_error().decode()
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, idx=P, q_pos=None, Sq=64, Sk=64, H=4, D=128, pool=4, topk=8,
+             scale=0.1, out=P, lse=P)
+    a.update(kw)
+    return D.lib().dsa_sparse_attn_fwd(a["q"], a["k"], a["v"], a["idx"], a["q_pos"], a["Sq"], a["Sk"],
+                                       a["H"], a["D"], a["pool"], a["topk"], a["scale"], a["out"],
+                                       a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(v=P + 4), 1, "v is not 16-byte aligned"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(D=64), 2, "head_dim=64"),
+    (dict(H=0), 2, "heads=0"),
+    (dict(H=17), 2, "heads=17"),
+    (dict(pool=2), 2, "pool=2"),
+    (dict(topk=2049), 2, "topk=2049"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(Sq=100), 1, "Sq=100 > Sk=64"),
+])
+def test_fwd_validation(kw, status, msg):
+    assert _fwd(**kw) == status
+    assert msg in D.lib().dsa_last_error().decode()
+
+
+def test_bwd_validation():
+    L = D.lib()
+    args = [P, P, P, P, P, P, P, None, 64, 64, 4, 128, 4, 8, 0.1, P, P, P, P, 1 << 40, None]
+    a = list(args); a[4] = None
+    assert L.dsa_sparse_attn_bwd(*a) == 1 and b"dout is NULL" in L.dsa_last_error()
+    a = list(args); a[18] = None
+    assert L.dsa_sparse_attn_bwd(*a) == 1 and b"ws is NULL" in L.dsa_last_error()
+    a = list(args); a[19] = 1000
+    assert L.dsa_sparse_attn_bwd(*a) == 3 and b"ws_bytes=1000" in L.dsa_last_error()
+    a = list(args); a[11] = 256
+    assert L.dsa_sparse_attn_bwd(*a) == 2
+
+
+def test_python_binding_checks_dtypes():
+    import torch
+    q = torch.zeros(4, 4, 64, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        D.index_topk(q, q[:, 0], q[:, :, 0], topk=4)

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases are compared element by element over every row; the full-size
+workloads run in the launch configuration the benchmark times and are
+compared on sampled rows (and sampled keys for dK/dV), which the oracle
+computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_topk_amd as D
+import synthetic as syn
+from oracle import dsa_oracle as O
+from tests.parity import (LSE_ABS, assert_close, assert_idx_equal, dev_bf16, dev_i32, host_f64,
+                          note, sample_rows)
+
+pytestmark = pytest.mark.gpu
+SCALE = 1.0 / np.sqrt(128.0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    D.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits(x):
+    return syn.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _int_inputs(Sq, Sk, seed, heads=4):
+    rng = np.random.default_rng([seed, 1234])
+    return (_bits(rng.integers(-3, 4, size=(Sq, heads, 64))),
+            _bits(rng.integers(-3, 4, size=(Sk, 64))),
+            _bits(rng.integers(-3, 4, size=(Sq, heads))))
+
+
+def gpu_index(q_idx, k_idx, w_idx, topk, q_chunk=256, q_pos=None):
+    qp = None if q_pos is None else dev_i32(q_pos)
+    idx = D.index_topk(dev_bf16(q_idx), dev_bf16(k_idx), dev_bf16(w_idx), topk=topk,
+                       q_chunk=q_chunk, q_pos=qp)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# indexer + top-k: bit-exact
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 7, 8, 63, 64, 65, 127, 200, 511, 515])
+@pytest.mark.parametrize("topk", [1, 3, 8, 64])
+def test_index_tiny_sweep(S, topk):
+    q, k, w = _int_inputs(S, S, seed=S * 7 + topk)
+    note(f"index tiny S={S} topk={topk}")
+    got = gpu_index(q, k, w, topk)
+    ref = O.index_topk(q, k, w, None, topk, workers=1)
+    assert_idx_equal(f"idx S={S} k={topk}", got, ref)
+
+
+def test_index_s4k_full():
+    wl = syn.WORKLOADS["s4k"]
+    d = syn.make_inputs(wl, parts=("index",))
+    note("index s4k full")
+    got = gpu_index(d["q_idx"], d["k_idx"], d["w_idx"], wl.topk, wl.q_chunk)
+    ref = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], None, wl.topk)
+    assert_idx_equal("idx s4k", got, ref)
+
+
+@pytest.mark.parametrize("S,topk,heads", [(8192, 512, 4), (6000, 100, 3), (3001, 2048, 4),
+                                          (2050, 17, 1)])
+def test_index_compaction_and_heads(S, topk, heads):
+    q, k, w = _int_inputs(S, S, seed=S + topk, heads=heads)
+    note(f"index S={S} topk={topk} heads={heads}")
+    got = gpu_index(q, k, w, topk, q_chunk=512)
+    ref = O.index_topk(q, k, w, None, topk)
+    assert_idx_equal("idx", got, ref)
+
+
+def test_index_all_ties():
+    S, topk = 2048, 40
+    q, k, _ = _int_inputs(S, S, seed=3)
+    w = _bits(np.zeros((S, 4)))
+    got = gpu_index(q, k, w, topk)
+    ref = O.index_topk(q, k, w, None, topk)
+    assert_idx_equal("idx all ties", got, ref)
+    full = np.arange(topk)[None, :]
+    assert (got[4 * topk:] == full).all()
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_index_monotone_scores(direction):
+    # score(p) = p (or n-1-p): with increasing scores every pool beats the
+    # running threshold, so candidate lists fill and compact on every tile
+    S, topk = 3072, 64
+    n = S // 4
+    vals = np.arange(n) if direction > 0 else np.arange(n)[::-1]
+    dims = np.arange(64)
+    kp = np.clip(0.25 * vals[:, None] - 3.0 * dims[None, :], 0.0, 3.0)   # sum over dims = vals/4
+    k_idx = np.repeat(kp, 4, axis=0).astype(np.float32)
+    q = np.ones((S, 4, 64), np.float32)
+    w = np.ones((S, 4), np.float32)
+    q, k_idx, w = _bits(q), _bits(k_idx), _bits(w)
+    got = gpu_index(q, k_idx, w, topk)
+    ref = O.index_topk(q, k_idx, w, None, topk)
+    assert_idx_equal(f"idx monotone {direction}", got, ref)
+    last = S - 1
+    want = np.arange(n - topk, n) if direction > 0 else np.arange(topk)
+    assert got[last].tolist() == want.tolist()
+
+
+def test_index_chunk_invariance_repeat_and_positions():
+    S, topk = 4096, 128
+    q, k, w = _int_inputs(S, S, seed=11)
+    base = gpu_index(q, k, w, topk, q_chunk=256)
+    for qc in (1, 64, 4096):
+        assert np.array_equal(gpu_index(q, k, w, topk, q_chunk=qc), base)
+    assert np.array_equal(gpu_index(q, k, w, topk, q_chunk=256), base)
+    perm = np.random.default_rng(5).permutation(S)
+    got = gpu_index(q[perm], k, w[perm], topk, q_pos=perm)
+    assert np.array_equal(got, base[perm])
+    ref = O.index_topk(q, k, w, None, topk)
+    assert_idx_equal("idx 4096", base, ref)
+
+
+def test_index_subset_positions_sk_larger():
+    # queries are a strided subset of a longer sequence (Sk not a multiple of 4)
+    Sk, topk = 5003, 32
+    pos = np.arange(0, Sk, 7)[::-1].copy()
+    q, k, w = _int_inputs(pos.shape[0], Sk, seed=21)
+    got = gpu_index(q, k, w, topk, q_pos=pos)
+    ref = O.index_topk(q, k, w, pos, topk)
+    assert_idx_equal("idx subset", got, ref)
+
+
+# ---------------------------------------------------------------------------
+# attention: forward and backward
+
+
+def gpu_attn(d, idx, q_pos=None, bwd=True):
+    q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    qp = None if q_pos is None else dev_i32(q_pos)
+    ti = dev_i32(idx)
+    out, lse = D.sparse_attn_fwd(q, k, v, ti, q_pos=qp, scale=SCALE)
+    res = {"out": out, "lse": lse}
+    if bwd:
+        dq, dk, dv = D.sparse_attn_bwd(q, k, v, out, dev_bf16(d["dout"]), lse, ti, q_pos=qp,
+                                       scale=SCALE)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {n: host_f64(t) for n, t in res.items()}
+
+
+def _attn_inputs(Sq, Sk, H, seed):
+    rng = np.random.default_rng([seed, 77])
+    return {"q": _bits(rng.standard_normal((Sq, H, 128))), "k": _bits(rng.standard_normal((Sk, 128))),
+            "v": _bits(rng.standard_normal((Sk, 128))), "dout": _bits(rng.standard_normal((Sq, H, 128)))}
+
+
+def _check_attn(tag, got, d, idx, q_pos, bwd=True):
+    o, lse = O.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, q_pos, SCALE)
+    assert_close(f"{tag} O", got["out"], o)
+    assert_close(f"{tag} lse", got["lse"], lse, max_abs=LSE_ABS, mean_abs=LSE_ABS, rel=1e-4)
+    if bwd:
+        dq, dk, dv = O.sparse_attn_bwd(d["q"], d["k"], d["v"], d["dout"], idx, q_pos, SCALE)
+        assert_close(f"{tag} dq", got["dq"], dq)
+        assert_close(f"{tag} dk", got["dk"], dk)
+        assert_close(f"{tag} dv", got["dv"], dv)
+
+
+@pytest.mark.parametrize("S,H,topk", [(2048, 4, 32), (4096, 16, 512), (1031, 3, 16), (9, 1, 1),
+                                      (2053, 16, 128)])
+def test_pipeline_small(S, H, topk):
+    note(f"pipeline small S={S} H={H} topk={topk}")
+    q_idx, k_idx, w_idx = _int_inputs(S, S, seed=S + H)
+    idx = gpu_index(q_idx, k_idx, w_idx, topk)
+    ref_idx = O.index_topk(q_idx, k_idx, w_idx, None, topk)
+    assert_idx_equal("idx", idx, ref_idx)
+    d = _attn_inputs(S, S, H, seed=S * 3 + H)
+    got = gpu_attn(d, idx)          # the HIP pipeline runs on its own selection
+    _check_attn(f"S={S} H={H} k={topk}", got, d, ref_idx, None)
+
+
+def test_attention_random_selection_positions():
+    # a subset of queries of a longer sequence, shuffled, with a random valid
+    # selection; Sk not a multiple of 4
+    Sk, H, topk = 3001, 4, 24
+    pos = np.random.default_rng(2).permutation(Sk)[:1500]
+    idx = syn.random_selection((pos + 1) // 4, topk, seed=4)
+    d = _attn_inputs(pos.shape[0], Sk, H, seed=8)
+    got = gpu_attn(d, idx, q_pos=pos)
+    _check_attn("subset", got, d, idx, pos)
+
+
+def test_attention_skips_invalid_ids():
+    # ids outside [0, n_c) and -1 in the middle are skipped, as documented
+    S, H, topk = 400, 2, 8
+    pos = np.arange(S)
+    idx = syn.random_selection((pos + 1) // 4, topk, seed=5)
+    bad = idx.copy()
+    bad[::3, 1] = -1
+    bad[1::5, 2] = 10 ** 6
+    clean = np.full_like(bad, -1)
+    for r in range(S):
+        nc = (r + 1) // 4
+        keep = [p for p in bad[r] if 0 <= p < nc]
+        clean[r, :len(keep)] = keep
+    d = _attn_inputs(S, S, H, seed=9)
+    got = gpu_attn(d, bad)
+    _check_attn("invalid ids", got, d, clean, None)
+
+
+def test_dense_equivalence_against_torch():
+    # topk covering every pool gives causal dense attention (torch fp32 SDPA on GPU)
+    S, H = 512, 4
+    d = _attn_inputs(S, S, H, seed=12)
+    topk = S // 4
+    idx = np.full((S, topk), -1, np.int32)
+    for i in range(S):
+        idx[i, :(i + 1) // 4] = np.arange((i + 1) // 4)
+    got = gpu_attn(d, idx, bwd=False)
+    q = dev_bf16(d["q"]).float().permute(1, 0, 2).contiguous()
+    k = dev_bf16(d["k"]).float().unsqueeze(0).expand(H, -1, -1).contiguous()
+    v = dev_bf16(d["v"]).float().unsqueeze(0).expand(H, -1, -1).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=SCALE)
+    assert_close("dense O", got["out"], ref.permute(1, 0, 2).double().cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (launch configuration of the benchmark), sampled checks
+
+FULL = ["s32k", "s128k", "zigzag4", "s1m"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_pipeline_sampled(name):
+    wl = syn.WORKLOADS[name]
+    parts = ("index", "attn", "bwd") if wl.backward else ("index", "attn")
+    note(f"full {name}: generating inputs")
+    d = syn.make_inputs(wl, parts=parts)
+    qp = d["q_pos"]
+    dev = {k: dev_bf16(d[k]) for k in ("q_idx", "k_idx", "w_idx", "q", "k", "v")}
+    tq = None if qp is None else dev_i32(qp)
+    note(f"full {name}: GPU index + fwd{' + bwd' if wl.backward else ''}")
+    idx = D.index_topk(dev["q_idx"], dev["k_idx"], dev["w_idx"], topk=wl.topk, q_chunk=wl.q_chunk,
+                       q_pos=tq)
+    out, lse = D.sparse_attn_fwd(dev["q"], dev["k"], dev["v"], idx, q_pos=tq, scale=SCALE)
+    if wl.backward:
+        tdo = dev_bf16(d["dout"])
+        dq, dk, dv = D.sparse_attn_bwd(dev["q"], dev["k"], dev["v"], out, tdo, lse, idx, q_pos=tq,
+                                       scale=SCALE)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.sq, wl.topk, qp)
+    note(f"full {name}: oracle on {rows.shape[0]} sampled rows")
+    ref_idx = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], qp, wl.topk, rows=rows)
+    got_idx = idx[torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert_idx_equal(f"{name} idx", got_idx, ref_idx, rows)
+    # attention rows: the oracle uses its own selection for those rows
+    full_idx = np.zeros((wl.sq, wl.topk), np.int32)
+    full_idx[rows] = ref_idx
+    o_ref, lse_ref = O.sparse_attn_fwd(d["q"], d["k"], d["v"], full_idx, qp, SCALE, rows=rows)
+    sel = torch.from_numpy(rows).cuda()
+    assert_close(f"{name} O", host_f64(out[sel]), o_ref)
+    assert_close(f"{name} lse", host_f64(lse[sel]), lse_ref, max_abs=LSE_ABS, mean_abs=LSE_ABS, rel=1e-4)
+    if wl.backward:
+        dq_ref, _, _ = O.sparse_attn_bwd(d["q"], d["k"], d["v"], d["dout"], full_idx, qp, SCALE,
+                                         rows=rows, key_rows=np.empty(0, np.int64))
+        assert_close(f"{name} dq", host_f64(dq[sel]), dq_ref)
+        # properties that hold at any size: sum_j dV[j] = sum_{r,h} dO[r,h];
+        # sum_j dK[j] = scale * sum_{r,h} (sum_j dS) q = 0 up to bf16 rounding of O
+        sdv = host_f64(dv).sum(axis=0)
+        sdo = host_f64(tdo.float().sum(dim=(0, 1)))
+        assert_close(f"{name} sum dV", sdv, sdo, max_abs=0.5, mean_abs=0.2, rel=1e-3)
+        sdk = np.abs(host_f64(dk).sum(axis=0)).max()
+        note(f"  {name}: max |sum dK| = {sdk:.3e}")
+        assert sdk < 1.0
+
+
+@pytest.mark.parametrize("name", ["s128k", "zigzag4"])
+def test_full_size_backward_sampled_keys(name):
+    # dK/dV of sampled keys need every query that selected them: use a random
+    # valid selection (a legal input of the attention entry points) so the
+    # oracle can find those queries without running the indexer on all rows
+    wl = syn.WORKLOADS[name]
+    d = syn.make_inputs(wl, parts=("attn", "bwd"))
+    qp = d["q_pos"]
+    pos = np.arange(wl.sq) if qp is None else qp
+    note(f"full {name}: random selection")
+    idx = syn.random_selection((pos.astype(np.int64) + 1) // 4, wl.topk, seed=1)
+    got_t = {}
+    q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    tq = None if qp is None else dev_i32(qp)
+    ti = dev_i32(idx)
+    out, lse = D.sparse_attn_fwd(q, k, v, ti, q_pos=tq, scale=SCALE)
+    dq, dk, dv = D.sparse_attn_bwd(q, k, v, out, dev_bf16(d["dout"]), lse, ti, q_pos=tq, scale=SCALE)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    keys = np.unique(np.concatenate([rng.integers(0, wl.sk, 24), [0, 1, 5, int(pos.max()),
+                                                                   int(pos.max()) - 3, wl.sk - 1]]))
+    rows = sample_rows(wl.sq, wl.topk, qp, n_random=32)
+    note(f"full {name}: oracle bwd on {rows.shape[0]} rows, {keys.shape[0]} keys")
+    dq_ref, dk_ref, dv_ref = O.sparse_attn_bwd(d["q"], d["k"], d["v"], d["dout"], idx, qp, SCALE,
+                                               rows=rows, key_rows=keys)
+    sel = torch.from_numpy(rows).cuda()
+    ks = torch.from_numpy(keys).cuda()
+    assert_close(f"{name} dq", host_f64(dq[sel]), dq_ref)
+    assert_close(f"{name} dk", host_f64(dk[ks]), dk_ref)
+    assert_close(f"{name} dv", host_f64(dv[ks]), dv_ref)

@@ -342,3 +342,15 @@ def test_multiprocess_matches_single():
     a = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], None, 32, rows=np.arange(0, 2048, 7), workers=1)
     b = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], None, 32, rows=np.arange(0, 2048, 7), workers=4)
     assert np.array_equal(a, b)
+
+
+def test_no_complete_pool_rows():
+    # S < 4: no pool is complete, every id is padding and the key set is the
+    # query's own tokens 0..i (causal attention over the prefix)
+    for S in (1, 2, 3):
+        q = _bits(np.ones((S, 4, 64)))
+        k = _bits(np.ones((S, 64)))
+        idx = O.index_topk(q, k, _bits(np.ones((S, 4))), None, topk=2, workers=1)
+        assert (idx == -1).all()
+        for i in range(S):
+            assert O.key_positions(idx[i], i).tolist() == list(range(i + 1))
