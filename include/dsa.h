@@ -1,0 +1,173 @@
+/*
+ * dsa.h -- C ABI of one DeepSeek-Sparse-Attention (DSA) layer on MI355X (gfx950).
+ *
+ * The layer, as the source pages describe it:
+ *   - an indexer scores every causal query against pools of 4 consecutive
+ *     key tokens, so selection cost is quadratic while attention reads about
+ *     2048 keys per query ("SkyRL 将 GLM-5.3-Flash 训练上下文扩至 100 万 token",
+ *     section "模型与瓶颈");
+ *   - the top-k pools are kept as an int32 pool-index list, and GLM-5.3-Flash
+ *     attends 2051 keys (not 2048) with no positional encoding (same page,
+ *     section "四块优化 1. DSA 真稀疏"); the indexer is scored in query chunks
+ *     so its score matrix never exists in full (same section, and the Anyscale
+ *     blog "How Lila Sciences and Anyscale Scaled GLM-5.3-Flash Training...",
+ *     lessons paragraph);
+ *   - attention over the selected keys accumulates softmax blockwise with a
+ *     running max and sum, which equals the one-shot softmax (lesson "128K
+ *     的序列,激活放在哪?", section "改进二:Ring Attention / 上下文并行").
+ *
+ * Readings where the pages are silent (the whole library follows them):
+ *   - pool key = mean of the 4 token keys; a pool is a candidate for the query
+ *     at position i only when complete: p < floor((i+1)/4);
+ *   - score(i,p) = sum_h w[i,h] * max(0, q_idx[i,h,:] . kpool[p,:]);
+ *   - top-k: descending score, equal scores go to the lower pool id, -0 = +0;
+ *   - keys(i) = tokens of the selected pools plus the query's own incomplete
+ *     pool (positions 4*floor((i+1)/4) .. i), so at most 4k+3 keys;
+ *   - softmax(scale * q.k) over keys(i) with one K/V head shared by all heads
+ *     (MQA); LSE in natural log.
+ *
+ * Conventions common to every entry point:
+ *   - Every tensor is dense, row-major and contiguous in device memory.
+ *     bf16 tensors are passed as raw 16-bit bfloat16 values.  Every device
+ *     pointer except q_pos must be 16-byte aligned; q_pos 4-byte aligned.
+ *   - q_pos: NULL means query row r sits at position r (then Sq <= Sk);
+ *     otherwise q_pos[r] is the global position of row r, 0 <= q_pos[r] < Sk,
+ *     in any order.  q_pos lives in device memory and is read by the kernels
+ *     (its range is the caller's contract; out-of-range values are clamped
+ *     to [0, Sk-1] on the device so no access leaves the buffers).
+ *   - Pool ids are global: pool p holds tokens 4p..4p+3.
+ *   - All work is enqueued on `stream` (NULL = the default stream); calls
+ *     return without synchronising.  Inputs must stay valid until the stream
+ *     has executed the call.
+ *   - The caller allocates and owns every buffer, including workspaces; the
+ *     library allocates no device memory, keeps no state between calls,
+ *     never writes its inputs and overwrites its outputs completely.  Calls
+ *     from several host threads are safe; two calls that share an output or
+ *     workspace buffer on different streams race.
+ *   - Arguments are validated on the host before any HIP call.  Unsupported
+ *     shapes return DSA_UNSUPPORTED_SHAPE: there is no fallback path (dense or
+ *     otherwise).  No exception crosses the ABI and nothing is printed;
+ *     dsa_last_error() gives the detail text of the calling thread's last
+ *     failure.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum dsa_status {
+  DSA_OK = 0,
+  DSA_INVALID_ARG = 1,          /* null or misaligned pointer, bad count      */
+  DSA_UNSUPPORTED_SHAPE = 2,    /* shape outside what the kernels implement   */
+  DSA_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below the matching *_ws_bytes()   */
+  DSA_HIP_ERROR = 4             /* a kernel launch failed (hipGetLastError)   */
+};
+
+/* Library version, major*10000 + minor*100 + patch. */
+int dsa_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* dsa_status_string(int status);
+
+/* Detail of the calling thread's last failed call ("" if none). The string
+ * is owned by the library and valid until the thread's next call. */
+const char* dsa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Indexer + top-k pool selection.
+ *
+ * Computes, for every query row r at position i, the top `topk` complete
+ * pools by indexer score (readings above) and writes their ids ascending to
+ * idx_out[r, 0..m), m = min(topk, floor((i+1)/4)), then -1 to idx_out[r, m..topk).
+ * Scores never reach device memory: the kernel keeps them on chip and only
+ * streams candidate pool ids whose score beats a running per-query threshold.
+ * Scoring is done in fp32 from bf16 products (bf16 pooled keys); for integer
+ * indexer inputs in [-3, 3] every value is exact, so results equal the exact
+ * real-number ranking.
+ *
+ *   q_idx   [Sq, idx_heads, idx_dim] bf16   indexer queries
+ *   k_idx   [Sk, idx_dim]            bf16   indexer keys (one per token)
+ *   w_idx   [Sq, idx_heads]          bf16   per-query head weights
+ *   q_pos   [Sq] int32 or NULL              see conventions
+ *   idx_out [Sq, topk]               int32  output
+ *   ws      workspace of ws_bytes >= dsa_index_topk_ws_bytes(...) bytes
+ *
+ * Supported: idx_dim == 64, 1 <= idx_heads <= 4, pool == 4,
+ * 1 <= topk <= 2048, q_chunk >= 1, 1 <= Sq, 1 <= Sk < 2^31.
+ * q_chunk is the query chunk: the queries that share one pass over the pool
+ * keys.  The kernel scores chunks in sub-tiles of 64 queries; the result
+ * does not depend on q_chunk.
+ */
+size_t dsa_index_topk_ws_bytes(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim,
+                               int32_t pool, int32_t topk, int32_t q_chunk);
+
+int dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_idx,
+                   const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t idx_heads,
+                   int32_t idx_dim, int32_t pool, int32_t topk, int32_t q_chunk,
+                   int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse attention forward.
+ *
+ * For every query row r at position i and head h:
+ *   O[r,h]   = sum_{j in keys(i)} softmax_j(scale * q[r,h].k[j]) * v[j]
+ *   lse[r,h] = log sum_{j in keys(i)} exp(scale * q[r,h].k[j])
+ * keys(i) = tokens 4p..4p+3 of every id p in idx[r,:] with 0 <= p <
+ * floor((i+1)/4), plus positions 4*floor((i+1)/4) .. i.  Ids outside that
+ * range (the -1 padding included) are skipped; ids must be distinct.
+ * Accumulation is fp32 with a running max (online softmax); O is rounded to
+ * bf16 (nearest even).
+ *
+ *   q   [Sq, heads, head_dim] bf16      k, v [Sk, head_dim] bf16 (shared)
+ *   idx [Sq, topk] int32                q_pos [Sq] int32 or NULL
+ *   out [Sq, heads, head_dim] bf16      lse [Sq, heads] fp32
+ *
+ * Supported: head_dim == 128, 1 <= heads <= 16, pool == 4,
+ * 1 <= topk <= 2048, 1 <= Sq, 1 <= Sk < 2^31.  scale must be finite and > 0.
+ */
+int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
+                        const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads,
+                        int32_t head_dim, int32_t pool, int32_t topk, float scale,
+                        void* out, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse attention backward.
+ *
+ * Gradients of L = sum(dout * O) for the forward above, with
+ *   P = exp(scale * q.k - lse),  Delta[r,h] = sum_d dout[r,h,d] * out[r,h,d],
+ *   dS = P * (dout.v - Delta),
+ *   dq[r,h] = scale * sum_j dS_j k[j]                     (written directly)
+ *   dk[j]  += scale * sum_{r,h} dS q[r,h],  dv[j] += sum_{r,h} P dout[r,h]
+ * dk/dv are accumulated in fp32 in the workspace with device atomics (their
+ * summation order is therefore not fixed) and then rounded to bf16 into
+ * dk/dv, which are overwritten; keys no query attends get 0.
+ *
+ *   q, out, dout [Sq, heads, head_dim] bf16   k, v [Sk, head_dim] bf16
+ *   lse [Sq, heads] fp32 (from the forward)   idx, q_pos as in the forward
+ *   dq [Sq, heads, head_dim] bf16             dk, dv [Sk, head_dim] bf16
+ *   ws  workspace of ws_bytes >= dsa_sparse_attn_bwd_ws_bytes(...) bytes
+ *
+ * Supported: as the forward.
+ */
+size_t dsa_sparse_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t heads, int32_t head_dim);
+
+int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, const int32_t* idx,
+                        const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads,
+                        int32_t head_dim, int32_t pool, int32_t topk, float scale,
+                        void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* DSA_H_ */

@@ -1,0 +1,204 @@
+"""Python binding of libdsa.so: one DeepSeek-Sparse-Attention layer on MI355X.
+
+Thin ctypes marshalling over the C ABI in include/dsa.h: every step of the
+layer runs in the HIP kernels of the library.  PyTorch provides device memory
+and the current stream only.  There is no fallback: if the library is not
+built, importing works but every call raises DsaLibraryMissing.
+
+    idx = index_topk(q_idx, k_idx, w_idx, topk=512, q_chunk=256, q_pos=None)
+    out, lse = sparse_attn_fwd(q, k, v, idx, q_pos=None, scale=None)
+    dq, dk, dv = sparse_attn_bwd(q, k, v, out, dout, lse, idx, q_pos=None, scale=None)
+
+Shapes: q_idx [Sq, 4, 64], k_idx [Sk, 64], w_idx [Sq, 4] (bf16); q [Sq, H, 128],
+k, v [Sk, 128] (bf16); idx [Sq, topk] int32; q_pos [Sq] int32 or None.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+HEAD_DIM = 128
+IDX_DIM = 64
+POOL = 4
+
+STATUS = {0: "DSA_OK", 1: "DSA_INVALID_ARG", 2: "DSA_UNSUPPORTED_SHAPE",
+          3: "DSA_WORKSPACE_TOO_SMALL", 4: "DSA_HIP_ERROR"}
+
+# (name, restype, argtypes) of every symbol include/dsa.h declares
+_P, _I64, _I32, _F, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "dsa_version": (ctypes.c_int, []),
+    "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dsa_last_error": (ctypes.c_char_p, []),
+    "dsa_index_topk_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32, _I32]),
+    "dsa_index_topk": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32,
+                                      _P, _P, _SZ, _P]),
+    "dsa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
+                                           _F, _P, _P, _P]),
+    "dsa_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32]),
+    "dsa_sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32,
+                                           _I32, _I32, _F, _P, _P, _P, _P, _SZ, _P]),
+}
+
+
+class DsaLibraryMissing(RuntimeError):
+    pass
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdsa.so (loading needs no GPU)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise DsaLibraryMissing(
+                f"{LIB_PATH} is not built; run `python -m long_context_sparse_topk_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DsaError(fn, status, lib().dsa_last_error().decode(errors="replace"))
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _want(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device: torch.device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _positions(q_pos, Sq, device):
+    if q_pos is None:
+        return None
+    _want(q_pos, "q_pos", torch.int32, 1, device)
+    if q_pos.shape[0] != Sq:
+        raise ValueError("q_pos must have Sq entries")
+    return q_pos
+
+
+def default_scale(head_dim: int = HEAD_DIM) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+# ---------------------------------------------------------------------------
+
+def index_topk_ws_bytes(Sq: int, Sk: int, topk: int, idx_heads: int = 4, q_chunk: int = 256) -> int:
+    return int(lib().dsa_index_topk_ws_bytes(Sq, Sk, idx_heads, IDX_DIM, POOL, topk, q_chunk))
+
+
+def sparse_attn_bwd_ws_bytes(Sq: int, Sk: int, heads: int) -> int:
+    return int(lib().dsa_sparse_attn_bwd_ws_bytes(Sq, Sk, heads, HEAD_DIM))
+
+
+def index_topk(q_idx, k_idx, w_idx, *, topk: int, q_chunk: int = 256, q_pos=None,
+               out=None, ws=None) -> torch.Tensor:
+    """Top-k pool ids [Sq, topk] int32, ascending, -1 padded."""
+    L = lib()
+    dev = q_idx.device
+    _want(q_idx, "q_idx", torch.bfloat16, 3, dev)
+    _want(k_idx, "k_idx", torch.bfloat16, 2, dev)
+    _want(w_idx, "w_idx", torch.bfloat16, 2, dev)
+    Sq, HI, DI = q_idx.shape
+    Sk = k_idx.shape[0]
+    if k_idx.shape[1] != DI or tuple(w_idx.shape) != (Sq, HI):
+        raise ValueError("indexer shapes disagree")
+    q_pos = _positions(q_pos, Sq, dev)
+    if out is None:
+        out = torch.empty((Sq, topk), dtype=torch.int32, device=dev)
+    else:
+        _want(out, "out", torch.int32, 2, dev)
+    need = int(L.dsa_index_topk_ws_bytes(Sq, Sk, HI, DI, POOL, topk, q_chunk))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = L.dsa_index_topk(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q_pos), Sq, Sk, HI, DI, POOL,
+                          topk, q_chunk, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream(dev))
+    _check("dsa_index_topk", st)
+    return out
+
+
+def sparse_attn_fwd(q, k, v, idx, *, q_pos=None, scale: float | None = None, out=None, lse=None):
+    """(out [Sq, H, 128] bf16, lse [Sq, H] fp32)."""
+    L = lib()
+    dev = q.device
+    _want(q, "q", torch.bfloat16, 3, dev)
+    _want(k, "k", torch.bfloat16, 2, dev)
+    _want(v, "v", torch.bfloat16, 2, dev)
+    _want(idx, "idx", torch.int32, 2, dev)
+    Sq, H, D = q.shape
+    Sk = k.shape[0]
+    if tuple(v.shape) != tuple(k.shape) or idx.shape[0] != Sq:
+        raise ValueError("attention shapes disagree")
+    q_pos = _positions(q_pos, Sq, dev)
+    scale = default_scale(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Sq, H), dtype=torch.float32, device=dev)
+    st = L.dsa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(q_pos), Sq, Sk, H, D, POOL,
+                               idx.shape[1], scale, _ptr(out), _ptr(lse), _stream(dev))
+    _check("dsa_sparse_attn_fwd", st)
+    return out, lse
+
+
+def sparse_attn_bwd(q, k, v, out, dout, lse, idx, *, q_pos=None, scale: float | None = None,
+                    ws=None, dq=None, dk=None, dv=None):
+    """(dq [Sq, H, 128], dk [Sk, 128], dv [Sk, 128]) bf16."""
+    L = lib()
+    dev = q.device
+    for t, n, nd in ((q, "q", 3), (k, "k", 2), (v, "v", 2), (out, "out", 3), (dout, "dout", 3)):
+        _want(t, n, torch.bfloat16, nd, dev)
+    _want(lse, "lse", torch.float32, 2, dev)
+    _want(idx, "idx", torch.int32, 2, dev)
+    Sq, H, D = q.shape
+    Sk = k.shape[0]
+    q_pos = _positions(q_pos, Sq, dev)
+    scale = default_scale(D) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(L.dsa_sparse_attn_bwd_ws_bytes(Sq, Sk, H, D))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = L.dsa_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(idx),
+                               _ptr(q_pos), Sq, Sk, H, D, POOL, idx.shape[1], scale, _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(dev))
+    _check("dsa_sparse_attn_bwd", st)
+    return dq, dk, dv

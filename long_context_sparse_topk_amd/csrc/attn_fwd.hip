@@ -1,0 +1,230 @@
+// Sparse attention forward over the selected pools (gfx950).
+//
+// What is computed (pages: "SkyRL 将 GLM-5.3-Flash 训练上下文扩至 100 万 token",
+// sections "模型与瓶颈" and "四块优化 1. DSA 真稀疏"; online softmax: lesson
+// "128K 的序列,激活放在哪?", section "改进二:Ring Attention / 上下文并行"):
+// each query attends, with no positional encoding, to the tokens of its
+// selected pools plus its own incomplete pool, all heads sharing one K/V head.
+// The softmax is accumulated tile by tile with a running max and sum.
+//
+// Mapping: one wave per query row, four rows per workgroup.  A tile is 8
+// pool slots = 32 keys.  Every gathered K/V row is a contiguous 256-byte
+// segment and every selected pool a contiguous 1 KiB segment of K (and of V).
+//   S^T[key, head] = K[key, :] . Q[head, :]      MFMA 16x16x32, keys as M
+//   O^T[dim, head] += V^T[dim, key] P^T[key, head]
+// The K rows are loaded straight into MFMA A-operand registers; V goes
+// through LDS to be read transposed.  With keys as M and heads as N, each lane
+// owns one head, so the online-softmax rescale is a per-lane scalar.
+
+#include "dsa_device.hpp"
+#include "dsa_kernels.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRows = 4;        // query rows (waves) per workgroup
+constexpr int kVStride = 136;   // LDS row stride (elements) of the V tile
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  const int32_t* q_pos;
+  int64_t Sq, Sk;
+  int H, topk;
+  float scale_log2;
+  uint16_t* out;
+  float* lse;
+};
+
+// Pool slot ps of a row: slots [0, np) are idx entries, slot np is the query's
+// own incomplete pool.  Returns the first key and the number of valid keys.
+__device__ __forceinline__ int2 slot_info(const int32_t* irow, int ps, int np, int nc, int part,
+                                          int pos) {
+  int base = pos, nv = 0;
+  if (ps < np) {
+    const int p = irow[ps];
+    if (p >= 0 && p < nc) {
+      base = 4 * p;
+      nv = 4;
+    }
+  } else if (ps == np && part > 0) {
+    base = 4 * nc;
+    nv = part;
+  }
+  return make_int2(base, nv);
+}
+
+__global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
+  __shared__ __align__(16) uint16_t lds_v[kRows][32 * kVStride];
+  __shared__ int2 lds_info[kRows][8];
+
+  const int lane = lane_id();
+  const int wave = uniform(threadIdx.x >> 6);
+  const int64_t r = (int64_t)blockIdx.x * kRows + wave;
+  if (r >= a.Sq) return;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const float NEG_INF = -__builtin_huge_valf();
+
+  int64_t pos64 = r;
+  if (a.q_pos) {
+    pos64 = a.q_pos[r];
+    pos64 = pos64 < 0 ? 0 : (pos64 >= a.Sk ? a.Sk - 1 : pos64);
+  }
+  const int pos = (int)pos64;
+  const int nc = (pos + 1) >> 2;
+  const int part = (pos + 1) & 3;
+  const int32_t* irow = a.idx + r * a.topk;
+
+  // pool slots to visit: up to the last non-negative id, then the own pool
+  int np = 0;
+  for (int j0 = 0; j0 < a.topk; j0 += kWave) {
+    const int j = j0 + lane;
+    const uint64_t M = ballot(j < a.topk && irow[j] >= 0);
+    if (M) np = j0 + 64 - __clzll((long long)M);
+  }
+  const int nps = np + (part > 0 ? 1 : 0);
+  const int ntile = (nps + 7) >> 3;
+
+  const bool hv = c16 < a.H;
+  bf16x8_t QB[4];
+  {
+    const uint16_t* src = a.q + (r * a.H + c16) * kD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) QB[ks] = hv ? load_bf16x8(src + 32 * ks) : zero_bf16x8();
+  }
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m2 = NEG_INF, lsum = 0.f;
+  uint16_t* vt = lds_v[wave];
+  int2* info = lds_info[wave];
+
+  for (int t = 0; t < ntile; ++t) {
+    if (lane < 8) info[lane] = slot_info(irow, 8 * t + lane, np, nc, part, pos);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    // K rows -> A operands; V rows -> LDS (same lane pattern)
+    bf16x8_t KA[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int2 in = info[4 * kb + (c16 >> 2)];
+      const int off = c16 & 3;
+      const int64_t key = off < in.y ? in.x + off : pos;
+      const uint16_t* ks_src = a.k + key * kD + 8 * g;
+      const uint16_t* vs_src = a.v + key * kD + 8 * g;
+      uint16_t* vdst = vt + (16 * kb + c16) * kVStride + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        KA[kb][ks] = load_bf16x8(ks_src + 32 * ks);
+        *reinterpret_cast<u32x4_t*>(vdst + 32 * ks) =
+            *reinterpret_cast<const u32x4_t*>(vs_src + 32 * ks);
+      }
+    }
+
+    f32x4_t S[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      S[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) S[kb] = mfma32(KA[kb][ks], QB[ks], S[kb]);
+    }
+
+    // lane holds keys 16*kb + 4*g + rr (pool slot 4*kb + g, offset rr) of head c16
+    float lg[8];
+    float tmax = NEG_INF;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int nv = info[4 * kb + g].y;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float x = rr < nv ? S[kb][rr] * a.scale_log2 : NEG_INF;
+        lg[4 * kb + rr] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float mnew = fmaxf(m2, tmax);
+    const float ms = mnew == NEG_INF ? 0.f : mnew;
+    const float alpha = exp2f(m2 - ms);
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = exp2f(lg[j] - ms);
+      psum += p[j];
+    }
+    lsum = lsum * alpha + psum;
+    m2 = mnew;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+
+    u32x4_t pb;
+    pb[0] = pack_bf16x2(p[0], p[1]);
+    pb[1] = pack_bf16x2(p[2], p[3]);
+    pb[2] = pack_bf16x2(p[4], p[5]);
+    pb[3] = pack_bf16x2(p[6], p[7]);
+    const bf16x8_t PB = as_bf16x8(pb);
+
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // V^T operand: row = dim 16*db + c16, k slot j -> key 4g+j (j<4) or 16+4g+(j-4)
+    const uint16_t* v0 = vt + (4 * g) * kVStride + c16;
+    const uint16_t* v1 = vt + (16 + 4 * g) * kVStride + c16;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      u32x4_t va;
+      va[0] = (uint32_t)v0[0 * kVStride + 16 * db] | ((uint32_t)v0[1 * kVStride + 16 * db] << 16);
+      va[1] = (uint32_t)v0[2 * kVStride + 16 * db] | ((uint32_t)v0[3 * kVStride + 16 * db] << 16);
+      va[2] = (uint32_t)v1[0 * kVStride + 16 * db] | ((uint32_t)v1[1 * kVStride + 16 * db] << 16);
+      va[3] = (uint32_t)v1[2 * kVStride + 16 * db] | ((uint32_t)v1[3 * kVStride + 16 * db] << 16);
+      acc[db] = mfma32(as_bf16x8(va), PB, acc[db]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  float lt = lsum + __shfl_xor(lsum, 16, kWave);
+  lt += __shfl_xor(lt, 32, kWave);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (hv) {
+    uint16_t* dst = a.out + (r * a.H + c16) * kD + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      u32x2_t o;
+      o[0] = pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv);
+      o[1] = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
+      *reinterpret_cast<u32x2_t*>(dst + 16 * db) = o;
+    }
+    if (g == 0) a.lse[r * a.H + c16] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : NEG_INF;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs& x, hipStream_t s) {
+  FwdArgs a;
+  a.q = x.q;
+  a.k = x.k;
+  a.v = x.v;
+  a.idx = x.idx;
+  a.q_pos = x.q_pos;
+  a.Sq = x.Sq;
+  a.Sk = x.Sk;
+  a.H = x.heads;
+  a.topk = x.topk;
+  a.scale_log2 = x.scale * kLog2e;
+  a.out = x.out;
+  a.lse = x.lse_out;
+  const int64_t blocks = (x.Sq + kRows - 1) / kRows;
+  attn_fwd_kernel<<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

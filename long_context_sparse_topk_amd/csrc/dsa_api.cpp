@@ -1,0 +1,219 @@
+// C ABI of the DSA layer: argument validation, workspace sizing and launches.
+//
+// Validation runs on the host before any HIP call and reports a specific
+// status; a shape the kernels do not implement is an error, never a silent
+// change of algorithm (the failure mode the SkyRL news item describes in
+// "四块优化 1. DSA 真稀疏": a fused sparse kernel that rejected the shape and
+// quietly fell back to dense attention).
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "dsa_kernels.hpp"
+
+#define DSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_ptr(const void* p, const char* name, size_t align) {
+  if (p == nullptr) return fail(DSA_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(DSA_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return DSA_OK;
+}
+
+constexpr int64_t kMaxSeq = (int64_t)1 << 31;
+
+int check_seq(int64_t Sq, int64_t Sk, const int32_t* q_pos) {
+  if (Sq < 1 || Sk < 1) return fail(DSA_INVALID_ARG, "Sq=%lld Sk=%lld must be >= 1", (long long)Sq, (long long)Sk);
+  if (Sq >= kMaxSeq || Sk >= kMaxSeq)
+    return fail(DSA_UNSUPPORTED_SHAPE, "Sq=%lld Sk=%lld must be < 2^31", (long long)Sq, (long long)Sk);
+  if (q_pos == nullptr && Sq > Sk)
+    return fail(DSA_INVALID_ARG, "q_pos is NULL (identity positions) but Sq=%lld > Sk=%lld",
+                (long long)Sq, (long long)Sk);
+  if (q_pos != nullptr && !aligned(q_pos, 4)) return fail(DSA_INVALID_ARG, "q_pos is not 4-byte aligned");
+  return DSA_OK;
+}
+
+int check_attn_shape(int64_t Sq, int64_t Sk, int32_t heads, int32_t head_dim, int32_t pool,
+                     int32_t topk, float scale, const int32_t* q_pos) {
+  int st = check_seq(Sq, Sk, q_pos);
+  if (st) return st;
+  if (head_dim != 128) return fail(DSA_UNSUPPORTED_SHAPE, "head_dim=%d (supported: 128)", head_dim);
+  if (heads < 1 || heads > 16) return fail(DSA_UNSUPPORTED_SHAPE, "heads=%d (supported: 1..16)", heads);
+  if (pool != 4) return fail(DSA_UNSUPPORTED_SHAPE, "pool=%d (supported: 4)", pool);
+  if (topk < 1 || topk > dsa::kMaxTopk)
+    return fail(DSA_UNSUPPORTED_SHAPE, "topk=%d (supported: 1..%d)", topk, dsa::kMaxTopk);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(DSA_INVALID_ARG, "scale must be finite and > 0");
+  return DSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+DSA_EXPORT int dsa_version(void) { return 100; }
+
+DSA_EXPORT const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_INVALID_ARG: return "invalid argument";
+    case DSA_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case DSA_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DSA_HIP_ERROR: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+DSA_EXPORT const char* dsa_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------------------
+
+DSA_EXPORT size_t dsa_index_topk_ws_bytes(int64_t Sq, int64_t Sk, int32_t idx_heads,
+                                          int32_t idx_dim, int32_t pool, int32_t topk,
+                                          int32_t q_chunk) {
+  (void)idx_heads; (void)idx_dim; (void)pool; (void)q_chunk;
+  if (Sq < 1 || Sk < 1 || topk < 1 || topk > dsa::kMaxTopk) return 0;
+  return dsa::index_ws_layout(Sq, Sk, topk).total;
+}
+
+DSA_EXPORT int dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_idx,
+                              const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t idx_heads,
+                              int32_t idx_dim, int32_t pool, int32_t topk, int32_t q_chunk,
+                              int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  int st;
+  if ((st = check_ptr(q_idx, "q_idx", 16))) return st;
+  if ((st = check_ptr(k_idx, "k_idx", 16))) return st;
+  if ((st = check_ptr(w_idx, "w_idx", 2))) return st;
+  if ((st = check_ptr(idx_out, "idx_out", 4))) return st;
+  if ((st = check_ptr(ws, "ws", 256))) return st;
+  if ((st = check_seq(Sq, Sk, q_pos))) return st;
+  if (idx_dim != 64) return fail(DSA_UNSUPPORTED_SHAPE, "idx_dim=%d (supported: 64)", idx_dim);
+  if (idx_heads < 1 || idx_heads > 4)
+    return fail(DSA_UNSUPPORTED_SHAPE, "idx_heads=%d (supported: 1..4)", idx_heads);
+  if (pool != 4) return fail(DSA_UNSUPPORTED_SHAPE, "pool=%d (supported: 4)", pool);
+  if (topk < 1 || topk > dsa::kMaxTopk)
+    return fail(DSA_UNSUPPORTED_SHAPE, "topk=%d (supported: 1..%d)", topk, dsa::kMaxTopk);
+  if (q_chunk < 1) return fail(DSA_INVALID_ARG, "q_chunk=%d must be >= 1", q_chunk);
+  const size_t need = dsa::index_ws_layout(Sq, Sk, topk).total;
+  if (ws_bytes < need)
+    return fail(DSA_WORKSPACE_TOO_SMALL, "ws_bytes=%zu < %zu", ws_bytes, need);
+
+  (void)hipGetLastError();
+  dsa::IndexArgs a;
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.k_idx = static_cast<const uint16_t*>(k_idx);
+  a.w_idx = static_cast<const uint16_t*>(w_idx);
+  a.q_pos = q_pos;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.heads = idx_heads;
+  a.topk = topk;
+  a.q_chunk = q_chunk;
+  a.idx_out = idx_out;
+  a.ws = ws;
+  return hip_status(dsa::launch_index_topk(a, stream), "dsa_index_topk launch");
+}
+
+DSA_EXPORT int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
+                                   const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads,
+                                   int32_t head_dim, int32_t pool, int32_t topk, float scale,
+                                   void* out, float* lse, hipStream_t stream) {
+  g_err[0] = '\0';
+  int st;
+  if ((st = check_ptr(q, "q", 16))) return st;
+  if ((st = check_ptr(k, "k", 16))) return st;
+  if ((st = check_ptr(v, "v", 16))) return st;
+  if ((st = check_ptr(idx, "idx", 4))) return st;
+  if ((st = check_ptr(out, "out", 16))) return st;
+  if ((st = check_ptr(lse, "lse", 4))) return st;
+  if ((st = check_attn_shape(Sq, Sk, heads, head_dim, pool, topk, scale, q_pos))) return st;
+
+  (void)hipGetLastError();
+  dsa::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = idx;
+  a.q_pos = q_pos;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.heads = heads;
+  a.topk = topk;
+  a.scale = scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse_out = lse;
+  return hip_status(dsa::launch_attn_fwd(a, stream), "dsa_sparse_attn_fwd launch");
+}
+
+DSA_EXPORT size_t dsa_sparse_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t heads,
+                                               int32_t head_dim) {
+  (void)Sq; (void)heads;
+  if (Sk < 1 || head_dim != 128) return 0;
+  return dsa::bwd_ws_bytes(Sk);
+}
+
+DSA_EXPORT int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, const int32_t* idx,
+                                   const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads,
+                                   int32_t head_dim, int32_t pool, int32_t topk, float scale,
+                                   void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  g_err[0] = '\0';
+  int st;
+  if ((st = check_ptr(q, "q", 16))) return st;
+  if ((st = check_ptr(k, "k", 16))) return st;
+  if ((st = check_ptr(v, "v", 16))) return st;
+  if ((st = check_ptr(out, "out", 16))) return st;
+  if ((st = check_ptr(dout, "dout", 16))) return st;
+  if ((st = check_ptr(lse, "lse", 4))) return st;
+  if ((st = check_ptr(idx, "idx", 4))) return st;
+  if ((st = check_ptr(dq, "dq", 16))) return st;
+  if ((st = check_ptr(dk, "dk", 16))) return st;
+  if ((st = check_ptr(dv, "dv", 16))) return st;
+  if ((st = check_ptr(ws, "ws", 256))) return st;
+  if ((st = check_attn_shape(Sq, Sk, heads, head_dim, pool, topk, scale, q_pos))) return st;
+  const size_t need = dsa::bwd_ws_bytes(Sk);
+  if (ws_bytes < need) return fail(DSA_WORKSPACE_TOO_SMALL, "ws_bytes=%zu < %zu", ws_bytes, need);
+
+  (void)hipGetLastError();
+  dsa::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse_in = lse;
+  a.idx = idx;
+  a.q_pos = q_pos;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.heads = heads;
+  a.topk = topk;
+  a.scale = scale;
+  a.out = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.ws = ws;
+  return hip_status(dsa::launch_attn_bwd(a, stream), "dsa_sparse_attn_bwd launch");
+}

@@ -1,0 +1,374 @@
+// Lightning indexer with a fused per-query top-k (gfx950).
+//
+// What is computed (pages: "SkyRL 将 GLM-5.3-Flash 训练上下文扩至 100 万 token",
+// sections "模型与瓶颈" and "四块优化 1. DSA 真稀疏"): every query is scored
+// against every complete 4-token pool of indexer keys and keeps the top-k pools
+// as an int32 id list.  The pages chunk the queries so the score matrix never
+// exists in full; here no score row leaves the chip at all.
+//
+// Kernels:
+//   pool_keys_kernel    kpool[p] = bf16(mean of k_idx[4p..4p+3])   (HBM-bound)
+//   indexer_topk_kernel per workgroup sub-tile of 64 queries (256 rows of
+//                       query x indexer-head), stream the causal pool range in
+//                       tiles of 64 pools staged in LDS; bf16 MFMA 16x16x32 gives
+//                       the 4 head dot products of a (query, pool) pair in one
+//                       lane, so ReLU, the head weights and the head sum are an
+//                       in-register epilogue.  Each score is compared with the
+//                       query's running threshold (the k-th best key so far);
+//                       survivors are appended, in pool order, to the query's
+//                       candidate list in the workspace.  When a list could
+//                       overflow, the owning wave selects its exact top-k with a
+//                       radix select over the order-preserving float keys and
+//                       compacts it stably, raising the threshold.  The final
+//                       list is already ascending in pool id.
+//
+// Exactness: pools are streamed in ascending id order and a candidate joins the
+// list only if its score is strictly greater than the threshold score, so an
+// equal score with a higher id loses exactly as the rule "ties go to the lower
+// pool id" demands; compaction breaks score ties by list position, which is
+// pool order.
+
+#include "dsa_device.hpp"
+#include "dsa_kernels.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int kDI = 64;              // indexer head dim
+constexpr int kQT = kIndexQueryTile; // 64 queries per sub-tile
+constexpr int kPT = kIndexPoolTile;  // 64 pools per staged tile
+constexpr int kWaves = 4;            // 16 queries per wave
+constexpr int kThreads = kWaves * kWave;
+
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restrict__ k_idx,
+                                                        uint16_t* __restrict__ kpool,
+                                                        int64_t n_pools) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_pools * 8) return;
+  const int64_t p = t >> 3;
+  const int c = (int)(t & 7);
+  const uint16_t* src = k_idx + (4 * p) * kDI + c * 8;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int tok = 0; tok < 4; ++tok) {
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + tok * kDI);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += bf16_to_f32(v[j] & 0xFFFFu);
+      acc[2 * j + 1] += bf16_to_f32(v[j] >> 16);
+    }
+  }
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[2 * j] * 0.25f, acc[2 * j + 1] * 0.25f);
+  *reinterpret_cast<u32x4_t*>(kpool + p * kDI + c * 8) = o;
+}
+
+// ---------------------------------------------------------------------------
+// exact top-k of one candidate list, wave-wide (all arguments wave-uniform).
+// Keeps the k largest keys, equal keys in list order, stably compacted to the
+// front of the list.  Returns the k-th largest key's float value.
+
+__device__ float select_and_compact(uint32_t* __restrict__ key, int32_t* __restrict__ pool,
+                                    int n, int k, uint32_t* hist) {
+  const int lane = lane_id();
+  __threadfence_block();  // candidate stores of every lane are visible
+
+  uint32_t o = 0u, an = 0xFFFFFFFFu;
+  for (int j = lane; j < n; j += kWave) {
+    const uint32_t x = key[j];
+    o |= x;
+    an &= x;
+  }
+  o = wave_or(o);
+  an = wave_and(an);
+  const uint32_t X = o ^ an;        // bits where the keys differ
+  uint32_t prefix = an & ~X;        // bits common to every key
+  int rem = k;                      // keys still to take among those in play
+
+  if (X != 0u) {
+    const int hi = 31 - __clz((int)X);
+    const int lo = __ffs((int)X) - 1;
+    int top = hi + 1;               // bits >= top of the answer are fixed in prefix
+    while (top > lo) {
+      const int width = min(8, top - lo);
+      const int shift = top - width;
+      const uint32_t dmask = (1u << width) - 1u;
+      const uint32_t hmask = top >= 32 ? 0u : (0xFFFFFFFFu << top);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0u;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      for (int j = lane; j < n; j += kWave) {
+        const uint32_t x = key[j];
+        if ((x & hmask) == (prefix & hmask)) atomicAdd(&hist[(x >> shift) & dmask], 1u);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const int h0 = (int)hist[lane * 4 + 0], h1 = (int)hist[lane * 4 + 1];
+      const int h2 = (int)hist[lane * 4 + 2], h3 = (int)hist[lane * 4 + 3];
+      const int tot = h0 + h1 + h2 + h3;
+      int suf = tot;  // inclusive suffix sum over lanes (bins ascending with lane)
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_down(suf, off, kWave);
+        if (lane + off < kWave) suf += t;
+      }
+      const uint64_t ge = ballot(suf >= rem);
+      const int L = 63 - __clzll((long long)ge);
+      const int s3 = suf - tot + h3, s2 = s3 + h2, s1 = s2 + h1;
+      int d, above;
+      if (s3 >= rem) { d = 3; above = s3 - h3; }
+      else if (s2 >= rem) { d = 2; above = s2 - h2; }
+      else if (s1 >= rem) { d = 1; above = s1 - h1; }
+      else { d = 0; above = suf - h0; }
+      const int digit = __shfl(lane * 4 + d, L, kWave);
+      above = __shfl(above, L, kWave);
+      rem -= above;
+      prefix |= (uint32_t)digit << shift;
+      top = shift;
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  // keep every key > T and the first `rem` keys == T, in list order
+  const uint32_t T = prefix;
+  int out = 0, eqseen = 0;
+  for (int j0 = 0; j0 < n; j0 += kWave) {
+    const int j = j0 + lane;
+    const bool in = j < n;
+    const uint32_t x = in ? key[j] : 0u;
+    const int32_t pp = in ? pool[j] : 0;
+    const bool gtf = in && x > T;
+    const bool eqf = in && x == T;
+    const uint64_t EQ = ballot(eqf);
+    const bool keep = gtf || (eqf && (eqseen + mbcnt(EQ)) < rem);
+    const uint64_t K = ballot(keep);
+    if (keep) {
+      const int dst = out + mbcnt(K);
+      key[dst] = x;
+      pool[dst] = pp;
+    }
+    out += __popcll(K);
+    eqseen += __popcll(EQ);
+  }
+  __threadfence_block();
+  return key_to_float(T);
+}
+
+// Tile order: each workgroup takes every gridDim-th tile, snaking, over tiles
+// ranked from the longest causal range down (the last query tiles when q_pos
+// is the identity).
+__device__ __forceinline__ int64_t snake_rank(int64_t it, int slot, int nslots) {
+  return (it & 1) ? it * nslots + (nslots - 1 - slot) : it * nslots + slot;
+}
+
+struct KernelArgs {
+  const uint16_t* q_idx;
+  const uint16_t* w_idx;
+  const uint16_t* kpool;
+  const int32_t* q_pos;
+  int64_t Sq, Sk;
+  int n_pools;
+  int heads, topk, cap;
+  int64_t ntiles;
+  uint32_t* cand_key;
+  int32_t* cand_pool;
+  int32_t* idx_out;
+};
+
+__global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a) {
+  __shared__ __align__(16) u32x4_t lds_k[kPT * 8];          // 64 pools x 128 B, swizzled
+  __shared__ uint32_t lds_hist[kWaves][256];
+  __shared__ int lds_np[kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = uniform(tid >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const int cap = a.cap;
+  const int topk = a.topk;
+  uint32_t* hist = lds_hist[wave];
+  const float NEG_INF = -__builtin_huge_valf();
+
+  for (int64_t it = 0;; ++it) {
+    const int64_t rank = snake_rank(it, blockIdx.x, gridDim.x);
+    if (rank >= a.ntiles) break;
+    const int64_t q0 = (a.ntiles - 1 - rank) * kQT;
+
+    // A operands: row (4*qq + h) of row block rb -> query 16*wave + 4*rb + qq, head h
+    bf16x8_t A[4][2];
+    float w[4][4];
+    int nc[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      {
+        const int64_t qr = q0 + 16 * wave + 4 * rb + (c16 >> 2);
+        const int h = c16 & 3;
+        const bool ok = qr < a.Sq && h < a.heads;
+        const uint16_t* src = a.q_idx + (qr * a.heads + h) * kDI + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) A[rb][ks] = ok ? load_bf16x8(src + 32 * ks) : zero_bf16x8();
+      }
+      {
+        const int64_t qr = q0 + 16 * wave + 4 * rb + g;
+        const bool ok = qr < a.Sq;
+        int64_t pos = qr;
+        if (ok && a.q_pos) {
+          pos = a.q_pos[qr];
+          pos = pos < 0 ? 0 : (pos >= a.Sk ? a.Sk - 1 : pos);
+        }
+        nc[rb] = ok ? (int)((pos + 1) >> 2) : 0;
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          w[rb][h] = (ok && h < a.heads) ? bf16_to_f32(a.w_idx[qr * a.heads + h]) : 0.f;
+      }
+    }
+    int ncm = max(max(nc[0], nc[1]), max(nc[2], nc[3]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ncm = max(ncm, __shfl_xor(ncm, o, kWave));
+    if (lane == 0) lds_np[wave] = ncm;
+    __syncthreads();
+    const int tp = max(max(lds_np[0], lds_np[1]), max(lds_np[2], lds_np[3]));
+
+    int cnt[4] = {0, 0, 0, 0};
+    float tau[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    const int64_t wbase = ((int64_t)blockIdx.x * kQT + 16 * wave) * cap;
+
+    u32x4_t pre[2];
+    auto gload = [&](int pt0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + kThreads * j;
+        const int pool = pt0 + (c >> 3);
+        u32x4_t z = {0u, 0u, 0u, 0u};
+        pre[j] = pool < a.n_pools
+                     ? *reinterpret_cast<const u32x4_t*>(a.kpool + (int64_t)pool * kDI + (c & 7) * 8)
+                     : z;
+      }
+    };
+    if (tp > 0) gload(0);
+
+    for (int pt0 = 0; pt0 < tp; pt0 += kPT) {
+      __syncthreads();  // previous tile's LDS reads are done
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + kThreads * j;
+        const int pr = c >> 3, ch = c & 7;
+        lds_k[pr * 8 + (ch ^ (pr & 7))] = pre[j];
+      }
+      __syncthreads();
+      if (pt0 + kPT < tp) gload(pt0 + kPT);
+
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int pr = 16 * cb + c16;
+        const bf16x8_t B0 = as_bf16x8(lds_k[pr * 8 + (g ^ (pr & 7))]);
+        const bf16x8_t B1 = as_bf16x8(lds_k[pr * 8 + ((4 + g) ^ (pr & 7))]);
+        const int pool = pt0 + pr;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mfma32(A[rb][0], B0, acc);
+          acc = mfma32(A[rb][1], B1, acc);
+          float s = w[rb][0] * fmaxf(acc[0], 0.f);
+          s = fmaf(w[rb][1], fmaxf(acc[1], 0.f), s);
+          s = fmaf(w[rb][2], fmaxf(acc[2], 0.f), s);
+          s = fmaf(w[rb][3], fmaxf(acc[3], 0.f), s);
+          s += 0.f;  // -0 -> +0
+          const bool sv = (pool < nc[rb]) && (s > tau[rb]);
+          const uint64_t M = ballot(sv);
+          if (M) {
+            const uint32_t gm = (uint32_t)(M >> (16 * g)) & 0xFFFFu;
+            if (sv) {
+              const int r = __popc(gm & ((1u << c16) - 1u));
+              const int64_t off = wbase + (int64_t)(4 * rb + g) * cap + cnt[rb] + r;
+              a.cand_key[off] = order_key(s);
+              a.cand_pool[off] = pool;
+            }
+            cnt[rb] += __popc(gm);
+          }
+        }
+      }
+
+      if (pt0 + kPT < tp) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          uint64_t need = ballot(cnt[rb] > cap - kPT);
+          while (need) {
+            const int L = __ffsll((long long)need) - 1;
+            const int gq = L >> 4;
+            need &= ~(0xFFFFull << (16 * gq));
+            const int n = __shfl(cnt[rb], L, kWave);
+            const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
+            const float T = select_and_compact(a.cand_key + base, a.cand_pool + base, n, topk, hist);
+            if (g == gq) {
+              cnt[rb] = topk;
+              tau[rb] = T;
+            }
+          }
+        }
+      }
+    }
+
+    // final selection and output
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      for (int gq = 0; gq < 4; ++gq) {
+        const int64_t qr = q0 + 16 * wave + 4 * rb + gq;
+        if (qr >= a.Sq) continue;
+        int n = __shfl(cnt[rb], 16 * gq, kWave);
+        const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
+        if (n > topk) {
+          select_and_compact(a.cand_key + base, a.cand_pool + base, n, topk, hist);
+          n = topk;
+        } else {
+          __threadfence_block();
+        }
+        int32_t* dst = a.idx_out + qr * topk;
+        for (int j = lane; j < topk; j += kWave) dst[j] = j < n ? a.cand_pool[base + j] : -1;
+      }
+    }
+    __syncthreads();  // lds_np reuse in the next tile
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
+  const IndexWorkspace L = index_ws_layout(ia.Sq, ia.Sk, ia.topk);
+  char* ws = static_cast<char*>(ia.ws);
+  uint16_t* kpool = reinterpret_cast<uint16_t*>(ws + L.kpool_off);
+  const int64_t n_pools = ia.Sk / 4;
+  if (n_pools > 0) {
+    const int64_t threads = n_pools * 8;
+    pool_keys_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(ia.k_idx, kpool,
+                                                                                 n_pools);
+  }
+  KernelArgs a;
+  a.q_idx = ia.q_idx;
+  a.w_idx = ia.w_idx;
+  a.kpool = kpool;
+  a.q_pos = ia.q_pos;
+  a.Sq = ia.Sq;
+  a.Sk = ia.Sk;
+  a.n_pools = (int)n_pools;
+  a.heads = ia.heads;
+  a.topk = ia.topk;
+  a.cap = index_candidate_cap(ia.topk);
+  a.ntiles = (ia.Sq + kQT - 1) / kQT;
+  a.cand_key = reinterpret_cast<uint32_t*>(ws + L.key_off);
+  a.cand_pool = reinterpret_cast<int32_t*>(ws + L.pool_off);
+  a.idx_out = ia.idx_out;
+  const int64_t slots = index_slots(ia.Sq);
+  indexer_topk_kernel<<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -178,18 +178,29 @@ _G: dict = {}
 def _workers(n_rows: int, workers: int | None) -> int:
     if workers is None:
         workers = min(16, os.cpu_count() or 1)
-    return max(1, min(int(workers), max(1, n_rows // 64)))
+    return max(1, min(int(workers), max(1, n_rows // 8)))
 
 
-def _run_rows(fn, rows: np.ndarray, workers: int | None):
-    """Map fn over row blocks; returns the list of block results in order."""
+def _single_thread_blas():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+
+
+def _run_rows(fn, rows: np.ndarray, workers: int | None, blocks_per_worker: int = 4):
+    """Map fn over row blocks; returns the list of block results in order.
+
+    Worker processes run single-threaded BLAS so that W workers use W cores.
+    """
     w = _workers(rows.shape[0], workers)
-    blocks = np.array_split(rows, max(w * 4, 1))
+    blocks = np.array_split(rows, max(w * blocks_per_worker, 1))
     blocks = [b for b in blocks if b.shape[0]]
     if w == 1:
         return [fn(b) for b in blocks]
     ctx = _mp.get_context("fork")
-    with ctx.Pool(w) as pool:
+    with ctx.Pool(w, initializer=_single_thread_blas) as pool:
         return pool.map(fn, blocks)
 
 
@@ -306,7 +317,7 @@ def sparse_attn_bwd(q, k, v, dout, idx, q_pos, scale: float, pool: int = 4,
     _G.clear()
     _G.update(q=q, k=k, v=v, dout=dout, idx=np.asarray(idx), pos=pos, pool=pool,
               scale=float(scale), key_rows=key_rows, key_slot=key_slot)
-    parts = _run_rows(_bwd_block, all_rows, workers)
+    parts = _run_rows(_bwd_block, all_rows, workers, blocks_per_worker=1)
     _G.clear()
     dq_all = np.concatenate([p[0] for p in parts]) if parts else np.empty((0,) + q.shape[1:])
     dk = sum((p[1] for p in parts), np.zeros((key_rows.shape[0], k.shape[1])))

@@ -4,6 +4,12 @@ Comparison bar: indices bit-exact; attention outputs and gradients within
 max |d| <= 2e-2 and mean |d| <= 2e-3 (bf16 I/O, fp32 accumulation), plus a
 relative-L2 bound of 1e-2 so that small-magnitude tensors cannot pass by
 being near zero.  LSE within 1e-3.
+
+The max-abs bound is applied to the error in excess of half a bf16 ulp of
+the value: rounding a correct result to bf16 alone moves values in [8, 16)
+by up to 2^-5 > 2e-2 (accumulated dK/dV of keys that many queries select
+reach that range), so no bf16 output could meet a bare 2e-2 there.  Below
+|x| = 4 half an ulp is at most 2^-7 and the bare bound dominates.
 """
 from __future__ import annotations
 
@@ -48,11 +54,16 @@ def assert_close(name: str, got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, m
     assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
     assert np.isfinite(got).all(), f"{name}: non-finite values"
     d = np.abs(got - ref)
-    mx, mn = float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+    mag = np.maximum(np.abs(got), np.abs(ref))
+    half_ulp = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 8), 0.0)
+    excess = np.maximum(d - half_ulp, 0.0)
+    mx, mn = float(excess.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+    raw = float(d.max()) if d.size else 0.0
     nr = float(np.linalg.norm(ref))
     rl = float(np.linalg.norm(got - ref) / nr) if nr > 0 else float(np.linalg.norm(got))
-    note(f"  {name}: max|d|={mx:.3e} mean|d|={mn:.3e} relL2={rl:.3e} (|ref|max={np.abs(ref).max():.3e})")
-    assert mx <= max_abs, f"{name}: max abs err {mx} > {max_abs}"
+    note(f"  {name}: max|d|={raw:.3e} (beyond bf16 half-ulp {mx:.3e}) mean|d|={mn:.3e} "
+         f"relL2={rl:.3e} (|ref|max={np.abs(ref).max():.3e})")
+    assert mx <= max_abs, f"{name}: max abs err beyond bf16 rounding {mx} > {max_abs}"
     assert mn <= mean_abs, f"{name}: mean abs err {mn} > {mean_abs}"
     assert rl <= rel, f"{name}: relative L2 err {rl} > {rel}"
 
