@@ -1,0 +1,303 @@
+"""Benchmark one DSA layer on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload s1m] [--secondary s128k]
+
+A step is one pass of the layer's hot path over one batch of synthetic input
+already resident in HBM: indexer + fused top-k, sparse attention forward, and
+the backward for workloads that train (s128k, zigzag4).  Prints one JSON line:
+tokens/s of the primary workload, the roofline of its dominant kernel
+(per-launch durations from HIP events on the launch stream), the CPU oracle
+timed on a bounded sample of the same workload, and the secondary workload's
+tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import long_context_sparse_topk_amd as D  # noqa: E402
+import synthetic as syn  # noqa: E402
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+BF16_PEAK = 2.5e15         # flop/s, dense bf16 MFMA
+SCALE = 1.0 / np.sqrt(128.0)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "attn_fwd_kernel": "long_context_sparse_topk_amd/csrc/attn_fwd.hip",
+    "indexer_topk_kernel": "long_context_sparse_topk_amd/csrc/indexer.hip",
+    "attn_bwd_kernel": "long_context_sparse_topk_amd/csrc/attn_bwd.hip",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per launch (per-unit figures: see the design notes)
+
+
+def positions(wl) -> np.ndarray:
+    qp = wl.q_positions()
+    return np.arange(wl.sq, dtype=np.int64) if qp is None else qp.astype(np.int64)
+
+
+def work(wl):
+    pos = positions(wl)
+    nc = (pos + 1) // 4
+    part = (pos + 1) % 4
+    nkeys = 4 * np.minimum(nc, wl.topk) + part
+    H, k = wl.heads, wl.topk
+    keys = int(nkeys.sum())
+    per_q_fwd = 2 * H * 128 * 2 + 4 * H + 4 * k
+    per_q_bwd = 4 * H * 128 * 2 + 4 * H + 4 * k
+    return {
+        "index_flop": 512 * int(nc.sum()),          # 4 heads x 64 dims x 2 per (query, pool)
+        "index_pairs": int(nc.sum()),
+        "keys": keys,
+        "fwd_bytes": 512 * keys + per_q_fwd * wl.sq,
+        "bwd_bytes": 1536 * keys + per_q_bwd * wl.sq,
+    }
+
+
+# ---------------------------------------------------------------------------
+
+
+class Layer:
+    """Inputs, outputs and workspaces of one workload, all resident on the GPU."""
+
+    def __init__(self, wl, device):
+        self.wl = wl
+        parts = ("index", "attn", "bwd") if wl.backward else ("index", "attn")
+        log(f"{wl.name}: generating inputs")
+        h = syn.make_inputs(wl, parts=parts)
+        self.host = h
+        dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(device)
+        self.t = {n: dev(h[n]) for n in parts_names(parts)}
+        self.q_pos = None if h["q_pos"] is None else torch.from_numpy(h["q_pos"]).to(device)
+        Sq, Sk, H, k = wl.sq, wl.sk, wl.heads, wl.topk
+        self.idx = torch.empty((Sq, k), dtype=torch.int32, device=device)
+        self.ws_idx = torch.empty(D.index_topk_ws_bytes(Sq, Sk, k, q_chunk=wl.q_chunk), dtype=torch.uint8,
+                                  device=device)
+        self.out = torch.empty((Sq, H, 128), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((Sq, H), dtype=torch.float32, device=device)
+        if wl.backward:
+            self.dq = torch.empty_like(self.out)
+            self.dk = torch.empty((Sk, 128), dtype=torch.bfloat16, device=device)
+            self.dv = torch.empty_like(self.dk)
+            self.ws_bwd = torch.empty(D.sparse_attn_bwd_ws_bytes(Sq, Sk, H), dtype=torch.uint8,
+                                      device=device)
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        t, wl = self.t, self.wl
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        D.index_topk(t["q_idx"], t["k_idx"], t["w_idx"], topk=wl.topk, q_chunk=wl.q_chunk,
+                     q_pos=self.q_pos, out=self.idx, ws=self.ws_idx)
+        rec(1)
+        D.sparse_attn_fwd(t["q"], t["k"], t["v"], self.idx, q_pos=self.q_pos, scale=SCALE,
+                          out=self.out, lse=self.lse)
+        rec(2)
+        if wl.backward:
+            D.sparse_attn_bwd(t["q"], t["k"], t["v"], self.out, t["dout"], self.lse, self.idx,
+                              q_pos=self.q_pos, scale=SCALE, ws=self.ws_bwd, dq=self.dq, dk=self.dk,
+                              dv=self.dv)
+            rec(3)
+
+
+def parts_names(parts):
+    names = []
+    if "index" in parts:
+        names += ["q_idx", "k_idx", "w_idx"]
+    if "attn" in parts:
+        names += ["q", "k", "v"]
+    if "bwd" in parts:
+        names += ["dout"]
+    return names
+
+
+def run(layer: Layer, steps: int, warmup: int):
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    n_ev = 4 if layer.wl.backward else 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        layer.step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {"index": [], "fwd": [], "bwd": []}
+    for e in evs:
+        per["index"].append(e[0].elapsed_time(e[1]) / 1e3)
+        per["fwd"].append(e[1].elapsed_time(e[2]) / 1e3)
+        if layer.wl.backward:
+            per["bwd"].append(e[2].elapsed_time(e[3]) / 1e3)
+    avg = {k: float(np.mean(v)) for k, v in per.items() if v}
+    return wall, avg
+
+
+def source_hash(rel: str) -> str:
+    h = hashlib.sha256()
+    for f in (rel, "long_context_sparse_topk_amd/csrc/dsa_device.hpp",
+              "long_context_sparse_topk_amd/csrc/dsa_kernels.hpp"):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter runs, or None when the
+    kernel source changed since they were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kernel][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(layer: Layer, budget_rows: int):
+    """The oracle as it stands on a random sample of query rows of the same
+    workload (indexer + top-k, forward, and backward dq for training
+    workloads); tokens/s = rows / seconds."""
+    from oracle import dsa_oracle as O
+    wl, h = layer.wl, layer.host
+    rng = np.random.default_rng(2024)
+    rows = np.sort(rng.choice(wl.sq, size=min(budget_rows, wl.sq), replace=False))
+    workers = min(16, os.cpu_count() or 1)
+    qp = h["q_pos"]
+    t0 = time.perf_counter()
+    sel = O.index_topk(h["q_idx"], h["k_idx"], h["w_idx"], qp, wl.topk, rows=rows, workers=workers)
+    full = np.zeros((wl.sq, wl.topk), np.int32)
+    full[rows] = sel
+    O.sparse_attn_fwd(h["q"], h["k"], h["v"], full, qp, SCALE, rows=rows, workers=workers)
+    if wl.backward:
+        O.sparse_attn_bwd(h["q"], h["k"], h["v"], h["dout"], full, qp, SCALE, rows=rows,
+                          key_rows=np.empty(0, np.int64), workers=workers)
+    dt = time.perf_counter() - t0
+    what = "index+top-k, fwd" + (", bwd (dq)" if wl.backward else "")
+    return {"value": rows.shape[0] / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{rows.shape[0]} random query rows of {wl.name} ({what}); "
+                      f"{dt:.2f} s wall on {workers} worker processes"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="s1m", choices=sorted(syn.WORKLOADS))
+    ap.add_argument("--secondary", default="s128k", help="second workload timed in the same run ('' = none)")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle sample size (rows)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer's sharding is a design note, not code). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        sys.exit(2)
+    D.lib()
+    device = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    wl = syn.WORKLOADS[args.workload]
+    layer = Layer(wl, device)
+    log(f"{wl.name}: warmup {args.warmup}, timed {args.steps}")
+    wall, avg = run(layer, args.steps, args.warmup)
+    w = work(wl)
+    step_s = wall / args.steps
+    value = wl.sq / step_s
+
+    # dominant kernel of the step and its roofline
+    kern = {
+        "indexer_topk_kernel": {"s": avg["index"], "bound": "mfma", "achieved": w["index_flop"] / avg["index"] / 1e12,
+                                "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s"},
+        "attn_fwd_kernel": {"s": avg["fwd"], "bound": "hbm", "achieved": w["fwd_bytes"] / avg["fwd"] / 1e9,
+                            "peak": HBM_PEAK / 1e9, "unit": "GB/s"},
+    }
+    if wl.backward:
+        kern["attn_bwd_kernel"] = {"s": avg["bwd"], "bound": "hbm",
+                                   "achieved": w["bwd_bytes"] / avg["bwd"] / 1e9,
+                                   "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    dom = max(kern, key=lambda n: kern[n]["s"])
+    dk = kern[dom]
+    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": round(dk["achieved"], 2), "peak": dk["peak"],
+                "unit": dk["unit"], "frac": round(dk["achieved"] / dk["peak"], 4),
+                "traffic": measured_traffic(dom, wl.name), "ms_per_launch": round(dk["s"] * 1e3, 3)}
+    kernels = {n: {"ms": round(v["s"] * 1e3, 3), "achieved": round(v["achieved"], 2), "unit": v["unit"],
+                   "frac": round(v["achieved"] / v["peak"], 4)} for n, v in kern.items()}
+
+    secondary = None
+    if args.secondary and args.secondary != wl.name:
+        sw = syn.WORKLOADS[args.secondary]
+        sl = Layer(sw, device)
+        swall, savg = run(sl, args.steps, args.warmup)
+        sws = work(sw)
+        secondary = {"workload": sw.name, "tokens_per_s": round(sw.sq * args.steps / swall, 1),
+                     "ms_per_step": round(swall / args.steps * 1e3, 3),
+                     "pass": "index+fwd+bwd" if sw.backward else "index+fwd",
+                     "ms": {k: round(v * 1e3, 3) for k, v in savg.items()},
+                     "index_mfma_frac": round(sws["index_flop"] / savg["index"] / BF16_PEAK, 4),
+                     "fwd_gather_GBps": round(sws["fwd_bytes"] / savg["fwd"] / 1e9, 1)}
+        if sw.backward:
+            secondary["bwd_GBps"] = round(sws["bwd_bytes"] / savg["bwd"] / 1e9, 1)
+        del sl
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline")
+        cpu = cpu_baseline(layer, args.cpu_rows)
+        cpu["value"] = round(cpu["value"], 2)
+
+    line = {
+        "metric": "DSA layer tokens/s (indexer + top-k + sparse attention fwd, +bwd when training)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "seq_len": wl.seq, "queries": wl.sq, "heads": wl.heads,
+                   "head_dim": 128, "indexer": "4x64", "pool": 4, "topk": wl.topk, "q_chunk": wl.q_chunk,
+                   "pass": "index+fwd+bwd" if wl.backward else "index+fwd", "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "index_mfma_frac": round(w["index_flop"] / avg["index"] / BF16_PEAK, 4),
+        "fwd_gather_GBps": round(w["fwd_bytes"] / avg["fwd"] / 1e9, 1),
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
