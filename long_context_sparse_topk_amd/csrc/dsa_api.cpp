@@ -13,7 +13,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "dsa_kernels.hpp"
 
 #define DSA_EXPORT extern "C" __attribute__((visibility("default")))

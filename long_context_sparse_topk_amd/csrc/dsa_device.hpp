@@ -83,6 +83,17 @@ __device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// orders global memory, which on this ISA (loads and stores share one
+// counter) waits for every global load in flight, prefetches included.
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
 // wave helpers
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }

@@ -13,9 +13,10 @@ constexpr int kIndexPoolTile = 64;      // pools per LDS-staged key tile
 constexpr int kIndexMaxSlots = 1024;    // resident workgroups owning candidate buffers
 constexpr int kMaxTopk = 2048;
 
-// per-query candidate capacity (multiple of 64, >= topk + one pool tile)
+// per-query candidate capacity (multiple of 64, >= topk + one pool tile):
+// each compaction absorbs about 2*topk survivors
 inline int index_candidate_cap(int topk) {
-  int c = 2 * topk;
+  int c = 3 * topk;
   if (c < topk + kIndexPoolTile) c = topk + kIndexPoolTile;
   return (c + 63) / 64 * 64;
 }
@@ -27,18 +28,23 @@ inline int64_t index_slots(int64_t Sq) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// pooled keys are stored padded to whole pool tiles (at least one tile)
+inline int64_t index_padded_pools(int64_t Sk) {
+  const int64_t n = Sk / 4;
+  const int64_t t = (n + kIndexPoolTile - 1) / kIndexPoolTile;
+  return (t > 0 ? t : 1) * kIndexPoolTile;
+}
+
 struct IndexWorkspace {
-  size_t kpool_off, key_off, pool_off, total;
+  size_t kpool_off, cand_off, total;
 };
 
 inline IndexWorkspace index_ws_layout(int64_t Sq, int64_t Sk, int topk) {
   IndexWorkspace w;
-  const int64_t n_pools = Sk / 4;
   const size_t cand = (size_t)index_slots(Sq) * kIndexQueryTile * index_candidate_cap(topk);
   w.kpool_off = 0;
-  w.key_off = align256((size_t)(n_pools > 0 ? n_pools : 1) * 64 * 2);
-  w.pool_off = w.key_off + align256(cand * 4);
-  w.total = w.pool_off + align256(cand * 4);
+  w.cand_off = align256((size_t)index_padded_pools(Sk) * 64 * 2);
+  w.total = w.cand_off + align256(cand * 8);
   return w;
 }
 

@@ -28,6 +28,8 @@
 // pool id" demands; compaction breaks score ties by list position, which is
 // pool order.
 
+#include <mutex>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -39,16 +41,23 @@ constexpr int kQT = kIndexQueryTile; // 64 queries per sub-tile
 constexpr int kPT = kIndexPoolTile;  // 64 pools per staged tile
 constexpr int kWaves = 4;            // 16 queries per wave
 constexpr int kThreads = kWaves * kWave;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer: 32-bit data format, no swizzle
 
 // ---------------------------------------------------------------------------
 
+// Pools [n_pools, n_padded) are zero-filled so that key tiles can be loaded
+// whole, without bounds predicates.
 __global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restrict__ k_idx,
                                                         uint16_t* __restrict__ kpool,
-                                                        int64_t n_pools) {
+                                                        int64_t n_pools, int64_t n_padded) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n_pools * 8) return;
+  if (t >= n_padded * 8) return;
   const int64_t p = t >> 3;
   const int c = (int)(t & 7);
+  if (p >= n_pools) {
+    *reinterpret_cast<u32x4_t*>(kpool + p * kDI + c * 8) = u32x4_t{0u, 0u, 0u, 0u};
+    return;
+  }
   const uint16_t* src = k_idx + (4 * p) * kDI + c * 8;
   float acc[8];
 #pragma unroll
@@ -71,18 +80,46 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // exact top-k of one candidate list, wave-wide (all arguments wave-uniform).
 // Keeps the k largest keys, equal keys in list order, stably compacted to the
-// front of the list.  Returns the k-th largest key's float value.
+// front of the list (or, with `out` set, written to `out` as pool ids).
+// Returns the k-th largest key's float value.  The caller has made the
+// wave's candidate stores visible (__threadfence_block) beforehand.
+//
+// The list is read in chunks of 64 x kR entries, keys and pool ids together,
+// with all loads of a lane in flight; a list of up to 64 x kR entries is read
+// once and stays in registers through every pass.  The k-th largest key is
+// found by a radix select over the bits where the keys differ (their OR xor
+// AND), 8 bits per pass, with a per-wave LDS histogram.
 
-__device__ float select_and_compact(uint32_t* __restrict__ key, int32_t* __restrict__ pool,
-                                    int n, int k, uint32_t* hist) {
+constexpr int kR = 24;
+constexpr int kChunk = kWave * kR;
+
+__device__ __forceinline__ void load_chunk(const u32x2_t* __restrict__ list, int base, int n,
+                                           u32x2_t (&e)[kR]) {
   const int lane = lane_id();
-  __threadfence_block();  // candidate stores of every lane are visible
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int j = base + i * kWave + lane;
+    e[i] = j < n ? list[j] : u32x2_t{0u, 0u};
+  }
+}
+
+__device__ float select_and_compact(u32x2_t* __restrict__ list, int n, int k, uint32_t* hist,
+                                    int32_t* __restrict__ out) {
+  const int lane = lane_id();
+  const int nch = (n + kChunk - 1) / kChunk;
+  u32x2_t e[kR];
+  if (nch == 1) load_chunk(list, 0, n, e);
 
   uint32_t o = 0u, an = 0xFFFFFFFFu;
-  for (int j = lane; j < n; j += kWave) {
-    const uint32_t x = key[j];
-    o |= x;
-    an &= x;
+  for (int c = 0; c < nch; ++c) {
+    if (nch > 1) load_chunk(list, c * kChunk, n, e);
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      if (c * kChunk + i * kWave + lane < n) {
+        o |= e[i][0];
+        an &= e[i][0];
+      }
+    }
   }
   o = wave_or(o);
   an = wave_and(an);
@@ -99,13 +136,18 @@ __device__ float select_and_compact(uint32_t* __restrict__ key, int32_t* __restr
       const int shift = top - width;
       const uint32_t dmask = (1u << width) - 1u;
       const uint32_t hmask = top >= 32 ? 0u : (0xFFFFFFFFu << top);
+      const uint32_t want = prefix & hmask;
 #pragma unroll
       for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0u;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      for (int j = lane; j < n; j += kWave) {
-        const uint32_t x = key[j];
-        if ((x & hmask) == (prefix & hmask)) atomicAdd(&hist[(x >> shift) & dmask], 1u);
+      for (int c = 0; c < nch; ++c) {
+        if (nch > 1) load_chunk(list, c * kChunk, n, e);
+#pragma unroll
+        for (int i = 0; i < kR; ++i) {
+          const bool in = c * kChunk + i * kWave + lane < n;
+          if (in && (e[i][0] & hmask) == want) atomicAdd(&hist[(e[i][0] >> shift) & dmask], 1u);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -138,26 +180,26 @@ __device__ float select_and_compact(uint32_t* __restrict__ key, int32_t* __restr
 
   // keep every key > T and the first `rem` keys == T, in list order
   const uint32_t T = prefix;
-  int out = 0, eqseen = 0;
-  for (int j0 = 0; j0 < n; j0 += kWave) {
-    const int j = j0 + lane;
-    const bool in = j < n;
-    const uint32_t x = in ? key[j] : 0u;
-    const int32_t pp = in ? pool[j] : 0;
-    const bool gtf = in && x > T;
-    const bool eqf = in && x == T;
-    const uint64_t EQ = ballot(eqf);
-    const bool keep = gtf || (eqf && (eqseen + mbcnt(EQ)) < rem);
-    const uint64_t K = ballot(keep);
-    if (keep) {
-      const int dst = out + mbcnt(K);
-      key[dst] = x;
-      pool[dst] = pp;
+  int kept = 0, eqseen = 0;
+  for (int c = 0; c < nch; ++c) {
+    if (nch > 1) load_chunk(list, c * kChunk, n, e);
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const bool in = c * kChunk + i * kWave + lane < n;
+      const bool gtf = in && e[i][0] > T;
+      const bool eqf = in && e[i][0] == T;
+      const uint64_t EQ = ballot(eqf);
+      const bool keep = gtf || (eqf && (eqseen + mbcnt(EQ)) < rem);
+      const uint64_t K = ballot(keep);
+      if (keep) {
+        const int dst = kept + mbcnt(K);
+        if (out) out[dst] = (int32_t)e[i][1];
+        else list[dst] = e[i];
+      }
+      kept += __popcll(K);
+      eqseen += __popcll(EQ);
     }
-    out += __popcll(K);
-    eqseen += __popcll(EQ);
   }
-  __threadfence_block();
   return key_to_float(T);
 }
 
@@ -177,13 +219,12 @@ struct KernelArgs {
   int n_pools;
   int heads, topk, cap;
   int64_t ntiles;
-  uint32_t* cand_key;
-  int32_t* cand_pool;
+  u32x2_t* cand;   // [slots][kQT][cap] (order key, pool id)
   int32_t* idx_out;
 };
 
 __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a) {
-  __shared__ __align__(16) u32x4_t lds_k[kPT * 8];          // 64 pools x 128 B, swizzled
+  __shared__ __align__(16) u32x4_t lds_k[2][kPT * 8];       // 2 x (64 pools x 128 B), swizzled
   __shared__ uint32_t lds_hist[kWaves][256];
   __shared__ int lds_np[kWaves];
 
@@ -233,81 +274,142 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     int ncm = max(max(nc[0], nc[1]), max(nc[2], nc[3]));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ncm = max(ncm, __shfl_xor(ncm, o, kWave));
+    int ncmin = min(min(nc[0], nc[1]), min(nc[2], nc[3]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ncmin = min(ncmin, __shfl_xor(ncmin, o, kWave));
+    ncmin = uniform(ncmin);
     if (lane == 0) lds_np[wave] = ncm;
-    __syncthreads();
+    lds_barrier();
     const int tp = max(max(lds_np[0], lds_np[1]), max(lds_np[2], lds_np[3]));
 
     int cnt[4] = {0, 0, 0, 0};
     float tau[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
     const int64_t wbase = ((int64_t)blockIdx.x * kQT + 16 * wave) * cap;
+    // this lane's query list of each row block: (order key, pool id) pairs
+    u32x2_t* clist[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) clist[rb] = a.cand + wbase + (int64_t)(4 * rb + g) * cap;
+    const uint32_t lane_below = (1u << c16) - 1u;
 
+    // pool-key tiles: global -> registers two tiles ahead, registers -> LDS
+    // one tile ahead (double buffer), one barrier per tile
+    // tile loads are unconditional (the pooled keys are padded to whole
+    // tiles) buffer loads: a per-tile resource in SGPRs and a loop-invariant
+    // per-thread offset, so no address registers are rewritten per tile
     u32x4_t pre[2];
     auto gload = [&](int pt0) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.kpool + (int64_t)pt0 * kDI), (short)0, kPT * kDI * 2, kBufferWord3);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = tid + kThreads * j;
-        const int pool = pt0 + (c >> 3);
-        u32x4_t z = {0u, 0u, 0u, 0u};
-        pre[j] = pool < a.n_pools
-                     ? *reinterpret_cast<const u32x4_t*>(a.kpool + (int64_t)pool * kDI + (c & 7) * 8)
-                     : z;
-      }
+      for (int j = 0; j < 2; ++j)
+        pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (tid + kThreads * j) * 16, 0, 0);
     };
-    if (tp > 0) gload(0);
-
-    for (int pt0 = 0; pt0 < tp; pt0 += kPT) {
-      __syncthreads();  // previous tile's LDS reads are done
+    auto lstore = [&](u32x4_t* buf) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int c = tid + kThreads * j;
         const int pr = c >> 3, ch = c & 7;
-        lds_k[pr * 8 + (ch ^ (pr & 7))] = pre[j];
+        buf[pr * 8 + (ch ^ (pr & 7))] = pre[j];
       }
-      __syncthreads();
-      if (pt0 + kPT < tp) gload(pt0 + kPT);
+    };
+    // tile 0 is always loaded (in bounds: the keys are padded to >= 1 tile),
+    // so every path into the loop has waited for the A operands
+    gload(0);
+    lstore(lds_k[0]);
+    if (kPT < tp) gload(kPT);
+    lds_barrier();
 
+    for (int t = 0, pt0 = 0; pt0 < tp; ++t, pt0 += kPT) {
+      const u32x4_t* kb = lds_k[t & 1];
+      // stage tile t+1 (loaded during the previous tile) into the other
+      // buffer, whose readers all passed the previous barrier; then start
+      // loading tile t+2
+      if (pt0 + kPT < tp) {
+        lstore(lds_k[(t + 1) & 1]);
+        if (pt0 + 2 * kPT < tp) gload(pt0 + 2 * kPT);
+      }
+
+      // 16 output blocks of 16 (query x head) rows x 16 pools
+      f32x4_t acc[4][4];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int pr = 16 * cb + c16;
-        const bf16x8_t B0 = as_bf16x8(lds_k[pr * 8 + (g ^ (pr & 7))]);
-        const bf16x8_t B1 = as_bf16x8(lds_k[pr * 8 + ((4 + g) ^ (pr & 7))]);
-        const int pool = pt0 + pr;
+        const bf16x8_t B0 = as_bf16x8(kb[pr * 8 + (g ^ (pr & 7))]);
+        const bf16x8_t B1 = as_bf16x8(kb[pr * 8 + ((4 + g) ^ (pr & 7))]);
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-          acc = mfma32(A[rb][0], B0, acc);
-          acc = mfma32(A[rb][1], B1, acc);
-          float s = w[rb][0] * fmaxf(acc[0], 0.f);
-          s = fmaf(w[rb][1], fmaxf(acc[1], 0.f), s);
-          s = fmaf(w[rb][2], fmaxf(acc[2], 0.f), s);
-          s = fmaf(w[rb][3], fmaxf(acc[3], 0.f), s);
-          s += 0.f;  // -0 -> +0
-          const bool sv = (pool < nc[rb]) && (s > tau[rb]);
-          const uint64_t M = ballot(sv);
-          if (M) {
-            const uint32_t gm = (uint32_t)(M >> (16 * g)) & 0xFFFFu;
-            if (sv) {
-              const int r = __popc(gm & ((1u << c16) - 1u));
-              const int64_t off = wbase + (int64_t)(4 * rb + g) * cap + cnt[rb] + r;
-              a.cand_key[off] = order_key(s);
-              a.cand_pool[off] = pool;
+          f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          acc[rb][cb] = mfma32(A[rb][1], B1, mfma32(A[rb][0], B0, z));
+        }
+      }
+      // epilogue: ReLU, head weights, head sum (branch-free)
+      float sc[4][4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const f32x4_t x = acc[rb][cb];
+          float s = w[rb][0] * fmaxf(x[0], 0.f);
+          s = fmaf(w[rb][1], fmaxf(x[1], 0.f), s);
+          s = fmaf(w[rb][2], fmaxf(x[2], 0.f), s);
+          sc[rb][cb] = fmaf(w[rb][3], fmaxf(x[3], 0.f), s);
+        }
+      }
+      // causal pool mask, only on tiles some query of the wave sees in part
+      if (pt0 + kPT > ncmin) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            if (pt0 + 16 * cb + c16 >= nc[rb]) sc[rb][cb] = NEG_INF;
+      }
+      // survivors: score strictly above the query's running threshold
+      uint64_t M[4][4];
+      uint64_t any = 0;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          M[rb][cb] = ballot(sc[rb][cb] > tau[rb]);
+          any |= M[rb][cb];
+        }
+      if (any) {
+        // append in pool order: per row block, column blocks ascending
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            if (M[rb][cb]) {
+              const uint32_t gm = (uint32_t)(M[rb][cb] >> (16 * g)) & 0xFFFFu;
+              if ((gm >> c16) & 1u) {
+                const int slot = __popc(gm & lane_below) + cnt[rb];
+                u32x2_t e;
+                e[0] = order_key(sc[rb][cb] + 0.f);  // -0 -> +0
+                e[1] = (uint32_t)(pt0 + 16 * cb + c16);
+                clist[rb][slot] = e;
+              }
+              cnt[rb] += __popc(gm);
             }
-            cnt[rb] += __popc(gm);
           }
         }
       }
 
       if (pt0 + kPT < tp) {
+        bool fenced = false;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           uint64_t need = ballot(cnt[rb] > cap - kPT);
+          if (need && !fenced) {
+            __threadfence_block();  // this wave's candidate stores are visible
+            fenced = true;
+          }
           while (need) {
             const int L = __ffsll((long long)need) - 1;
             const int gq = L >> 4;
             need &= ~(0xFFFFull << (16 * gq));
             const int n = __shfl(cnt[rb], L, kWave);
             const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
-            const float T = select_and_compact(a.cand_key + base, a.cand_pool + base, n, topk, hist);
+            const float T = select_and_compact(a.cand + base, n, topk, hist, nullptr);
             if (g == gq) {
               cnt[rb] = topk;
               tau[rb] = T;
@@ -315,28 +417,66 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
           }
         }
       }
+      lds_barrier();
     }
 
-    // final selection and output
+    // final selection, written straight to the output rows
+    __threadfence_block();
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       for (int gq = 0; gq < 4; ++gq) {
         const int64_t qr = q0 + 16 * wave + 4 * rb + gq;
         if (qr >= a.Sq) continue;
-        int n = __shfl(cnt[rb], 16 * gq, kWave);
+        const int n = __shfl(cnt[rb], 16 * gq, kWave);
         const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
-        if (n > topk) {
-          select_and_compact(a.cand_key + base, a.cand_pool + base, n, topk, hist);
-          n = topk;
-        } else {
-          __threadfence_block();
-        }
         int32_t* dst = a.idx_out + qr * topk;
-        for (int j = lane; j < topk; j += kWave) dst[j] = j < n ? a.cand_pool[base + j] : -1;
+        int filled = n;
+        if (n > topk) {
+          select_and_compact(a.cand + base, n, topk, hist, dst);
+          filled = topk;
+        } else {
+          const u32x2_t* src = a.cand + base;
+          for (int j0 = 0; j0 < n; j0 += 8 * kWave) {
+            int32_t v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int j = j0 + i * kWave + lane;
+              v[i] = j < n ? (int32_t)src[j][1] : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int j = j0 + i * kWave + lane;
+              if (j < n) dst[j] = v[i];
+            }
+          }
+        }
+        for (int j = filled + lane; j < topk; j += kWave) dst[j] = -1;
       }
     }
-    __syncthreads();  // lds_np reuse in the next tile
+    lds_barrier();  // lds_np reuse in the next tile
   }
+}
+
+// Workgroups the device keeps resident at once (cached per device): the
+// persistent grid is never larger, so no slot waits for another to finish.
+int resident_index_blocks() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kIndexMaxSlots;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, indexer_topk_kernel, kThreads, 0) !=
+            hipSuccess ||
+        cus * per <= 0) {
+      (void)hipGetLastError();
+      return kIndexMaxSlots;
+    }
+    cache[dev] = cus * per;
+  }
+  return cache[dev];
 }
 
 }  // namespace
@@ -346,10 +486,11 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   char* ws = static_cast<char*>(ia.ws);
   uint16_t* kpool = reinterpret_cast<uint16_t*>(ws + L.kpool_off);
   const int64_t n_pools = ia.Sk / 4;
-  if (n_pools > 0) {
-    const int64_t threads = n_pools * 8;
-    pool_keys_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(ia.k_idx, kpool,
-                                                                                 n_pools);
+  const int64_t n_padded = index_padded_pools(ia.Sk);
+  {
+    const int64_t threads = n_padded * 8;
+    pool_keys_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(
+        ia.k_idx, kpool, n_pools, n_padded);
   }
   KernelArgs a;
   a.q_idx = ia.q_idx;
@@ -363,10 +504,11 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   a.topk = ia.topk;
   a.cap = index_candidate_cap(ia.topk);
   a.ntiles = (ia.Sq + kQT - 1) / kQT;
-  a.cand_key = reinterpret_cast<uint32_t*>(ws + L.key_off);
-  a.cand_pool = reinterpret_cast<int32_t*>(ws + L.pool_off);
+  a.cand = reinterpret_cast<u32x2_t*>(ws + L.cand_off);
   a.idx_out = ia.idx_out;
-  const int64_t slots = index_slots(ia.Sq);
+  int64_t slots = index_slots(ia.Sq);  // the workspace holds candidate lists for this many
+  const int64_t resident = resident_index_blocks();
+  if (resident < slots) slots = resident;
   indexer_topk_kernel<<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
