@@ -36,7 +36,7 @@ inline int64_t index_padded_pools(int64_t Sk) {
 }
 
 struct IndexWorkspace {
-  size_t kpool_off, cand_off, total;
+  size_t kpool_off, cand_off, fb_off, total;
 };
 
 inline IndexWorkspace index_ws_layout(int64_t Sq, int64_t Sk, int topk) {
@@ -44,7 +44,8 @@ inline IndexWorkspace index_ws_layout(int64_t Sq, int64_t Sk, int topk) {
   const size_t cand = (size_t)index_slots(Sq) * kIndexQueryTile * index_candidate_cap(topk);
   w.kpool_off = 0;
   w.cand_off = align256((size_t)index_padded_pools(Sk) * 64 * 2);
-  w.total = w.cand_off + align256(cand * 8);
+  w.fb_off = w.cand_off + align256(cand * 8);          // fallback count + rows
+  w.total = w.fb_off + 256 + align256((size_t)Sq * 4);
   return w;
 }
 

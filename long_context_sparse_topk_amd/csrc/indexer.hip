@@ -28,6 +28,7 @@
 // pool id" demands; compaction breaks score ties by list position, which is
 // pool order.
 
+#include <cmath>
 #include <mutex>
 
 #include "dsa_device.hpp"
@@ -47,10 +48,13 @@ constexpr int kBufferWord3 = 0x00020000;  // raw buffer: 32-bit data format, no 
 
 // Pools [n_pools, n_padded) are zero-filled so that key tiles can be loaded
 // whole, without bounds predicates.
+// Thread 0 also clears the indexer's fallback-list length.
 __global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restrict__ k_idx,
                                                         uint16_t* __restrict__ kpool,
-                                                        int64_t n_pools, int64_t n_padded) {
+                                                        int64_t n_pools, int64_t n_padded,
+                                                        uint32_t* __restrict__ fb_count) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t == 0) *fb_count = 0u;
   if (t >= n_padded * 8) return;
   const int64_t p = t >> 3;
   const int c = (int)(t & 7);
@@ -218,11 +222,31 @@ struct KernelArgs {
   int64_t Sq, Sk;
   int n_pools;
   int heads, topk, cap;
-  int64_t ntiles;
-  u32x2_t* cand;   // [slots][kQT][cap] (order key, pool id)
+  int sample_stride;       // phase 1 streams every sample_stride-th pool tile
+  int sample_rank;         // r: phase 1 keeps the r-th best sampled score
+  const int32_t* rows;     // exact pass: rows to score (the fallback list)
+  const uint32_t* nrows;   // exact pass: device count of rows
+  uint32_t* fb_count;      // two-phase pass: fallback list length
+  int32_t* fb_rows;        // two-phase pass: fallback list
+  u32x2_t* cand;           // [slots][kQT][cap] (order key, pool id)
   int32_t* idx_out;
 };
 
+// largest float below x (x finite or -inf); +0 and -0 are one score
+__device__ __forceinline__ float float_below(float x) {
+  if (x == 0.f) return -__builtin_bit_cast(float, 1u);
+  if (x == -__builtin_huge_valf()) return x;
+  return key_to_float(order_key(x) - 1u);
+}
+
+// Two-phase pass (kTwoPhase): per query, phase 1 streams a strided sample of
+// the pool tiles and takes the exact r-th best sampled score t; phase 2
+// streams every tile keeping pools with score >= t, then the running top-k.
+// If at least min(k, n_c) pools score >= t, every true top-k pool does (its
+// score is >= the k-th best score >= t), so the result is exact; otherwise
+// the query goes to the fallback list, which the exact pass (!kTwoPhase:
+// one phase, threshold from -inf) then scores.
+template <bool kTwoPhase>
 __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a) {
   __shared__ __align__(16) u32x4_t lds_k[2][kPT * 8];       // 2 x (64 pools x 128 B), swizzled
   __shared__ uint32_t lds_hist[kWaves][256];
@@ -237,11 +261,17 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
   const int topk = a.topk;
   uint32_t* hist = lds_hist[wave];
   const float NEG_INF = -__builtin_huge_valf();
+  const int64_t nrow = kTwoPhase ? a.Sq : (int64_t)__builtin_amdgcn_readfirstlane(*a.nrows);
+  const int64_t ntiles = (nrow + kQT - 1) / kQT;
 
   for (int64_t it = 0;; ++it) {
     const int64_t rank = snake_rank(it, blockIdx.x, gridDim.x);
-    if (rank >= a.ntiles) break;
-    const int64_t q0 = (a.ntiles - 1 - rank) * kQT;
+    if (rank >= ntiles) break;
+    const int64_t q0 = (kTwoPhase ? ntiles - 1 - rank : rank) * kQT;
+    auto row_of = [&](int64_t i) -> int64_t {
+      if (i >= nrow) return -1;
+      return kTwoPhase ? i : (int64_t)a.rows[i];
+    };
 
     // A operands: row (4*qq + h) of row block rb -> query 16*wave + 4*rb + qq, head h
     bf16x8_t A[4][2];
@@ -250,16 +280,16 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       {
-        const int64_t qr = q0 + 16 * wave + 4 * rb + (c16 >> 2);
+        const int64_t qr = row_of(q0 + 16 * wave + 4 * rb + (c16 >> 2));
         const int h = c16 & 3;
-        const bool ok = qr < a.Sq && h < a.heads;
+        const bool ok = qr >= 0 && h < a.heads;
         const uint16_t* src = a.q_idx + (qr * a.heads + h) * kDI + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) A[rb][ks] = ok ? load_bf16x8(src + 32 * ks) : zero_bf16x8();
       }
       {
-        const int64_t qr = q0 + 16 * wave + 4 * rb + g;
-        const bool ok = qr < a.Sq;
+        const int64_t qr = row_of(q0 + 16 * wave + 4 * rb + g);
+        const bool ok = qr >= 0;
         int64_t pos = qr;
         if (ok && a.q_pos) {
           pos = a.q_pos[qr];
@@ -281,6 +311,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     if (lane == 0) lds_np[wave] = ncm;
     lds_barrier();
     const int tp = max(max(lds_np[0], lds_np[1]), max(lds_np[2], lds_np[3]));
+    const int ntp = (tp + kPT - 1) / kPT;   // pool tiles in the tile's causal range
 
     int cnt[4] = {0, 0, 0, 0};
     float tau[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
@@ -292,14 +323,13 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     const uint32_t lane_below = (1u << c16) - 1u;
 
     // pool-key tiles: global -> registers two tiles ahead, registers -> LDS
-    // one tile ahead (double buffer), one barrier per tile
-    // tile loads are unconditional (the pooled keys are padded to whole
-    // tiles) buffer loads: a per-tile resource in SGPRs and a loop-invariant
-    // per-thread offset, so no address registers are rewritten per tile
+    // one tile ahead (double buffer), one LDS-only barrier per tile.  The
+    // loads are unconditional raw buffer loads (the keys are padded to whole
+    // tiles) from a per-tile resource and a loop-invariant per-thread offset.
     u32x4_t pre[2];
-    auto gload = [&](int pt0) {
+    auto gload = [&](int tile) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.kpool + (int64_t)pt0 * kDI), (short)0, kPT * kDI * 2, kBufferWord3);
+          (void*)(a.kpool + (int64_t)tile * kPT * kDI), (short)0, kPT * kDI * 2, kBufferWord3);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (tid + kThreads * j) * 16, 0, 0);
@@ -312,122 +342,154 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         buf[pr * 8 + (ch ^ (pr & 7))] = pre[j];
       }
     };
-    // tile 0 is always loaded (in bounds: the keys are padded to >= 1 tile),
-    // so every path into the loop has waited for the A operands
-    gload(0);
-    lstore(lds_k[0]);
-    if (kPT < tp) gload(kPT);
-    lds_barrier();
 
-    for (int t = 0, pt0 = 0; pt0 < tp; ++t, pt0 += kPT) {
-      const u32x4_t* kb = lds_k[t & 1];
-      // stage tile t+1 (loaded during the previous tile) into the other
-      // buffer, whose readers all passed the previous barrier; then start
-      // loading tile t+2
-      if (pt0 + kPT < tp) {
-        lstore(lds_k[(t + 1) & 1]);
-        if (pt0 + 2 * kPT < tp) gload(pt0 + 2 * kPT);
-      }
-
-      // 16 output blocks of 16 (query x head) rows x 16 pools
-      f32x4_t acc[4][4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int pr = 16 * cb + c16;
-        const bf16x8_t B0 = as_bf16x8(kb[pr * 8 + (g ^ (pr & 7))]);
-        const bf16x8_t B1 = as_bf16x8(kb[pr * 8 + ((4 + g) ^ (pr & 7))]);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          acc[rb][cb] = mfma32(A[rb][1], B1, mfma32(A[rb][0], B0, z));
+    // Stream pool tiles first, first+step, ... < ntp, keeping each query's
+    // running top-klim.  Tile 0 of a stream is always loaded (in bounds: the
+    // keys are padded to >= 1 tile) so every path into the loop has waited
+    // for the A operands.
+    auto stream = [&](int first, int step, int klim) {
+      const int nt = first < ntp ? (ntp - first + step - 1) / step : 0;
+      gload(first < ntp ? first : 0);
+      lstore(lds_k[0]);
+      if (nt > 1) gload(first + step);
+      lds_barrier();
+      for (int i = 0; i < nt; ++i) {
+        const int pt0 = (first + i * step) * kPT;
+        const u32x4_t* kb = lds_k[i & 1];
+        if (i + 1 < nt) {
+          lstore(lds_k[(i + 1) & 1]);
+          if (i + 2 < nt) gload(first + (i + 2) * step);
         }
-      }
-      // epilogue: ReLU, head weights, head sum (branch-free)
-      float sc[4][4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+
+        // 16 output blocks of 16 (query x head) rows x 16 pools
+        f32x4_t acc[4][4];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          const f32x4_t x = acc[rb][cb];
-          float s = w[rb][0] * fmaxf(x[0], 0.f);
-          s = fmaf(w[rb][1], fmaxf(x[1], 0.f), s);
-          s = fmaf(w[rb][2], fmaxf(x[2], 0.f), s);
-          sc[rb][cb] = fmaf(w[rb][3], fmaxf(x[3], 0.f), s);
+          const int pr = 16 * cb + c16;
+          const bf16x8_t B0 = as_bf16x8(kb[pr * 8 + (g ^ (pr & 7))]);
+          const bf16x8_t B1 = as_bf16x8(kb[pr * 8 + ((4 + g) ^ (pr & 7))]);
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            acc[rb][cb] = mfma32(A[rb][1], B1, mfma32(A[rb][0], B0, z));
+          }
         }
-      }
-      // causal pool mask, only on tiles some query of the wave sees in part
-      if (pt0 + kPT > ncmin) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            if (pt0 + 16 * cb + c16 >= nc[rb]) sc[rb][cb] = NEG_INF;
-      }
-      // survivors: score strictly above the query's running threshold
-      uint64_t M[4][4];
-      uint64_t any = 0;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          M[rb][cb] = ballot(sc[rb][cb] > tau[rb]);
-          any |= M[rb][cb];
-        }
-      if (any) {
-        // append in pool order: per row block, column blocks ascending
+        // epilogue: ReLU, head weights, head sum (branch-free)
+        float sc[4][4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            if (M[rb][cb]) {
-              const uint32_t gm = (uint32_t)(M[rb][cb] >> (16 * g)) & 0xFFFFu;
-              if ((gm >> c16) & 1u) {
-                const int slot = __popc(gm & lane_below) + cnt[rb];
-                u32x2_t e;
-                e[0] = order_key(sc[rb][cb] + 0.f);  // -0 -> +0
-                e[1] = (uint32_t)(pt0 + 16 * cb + c16);
-                clist[rb][slot] = e;
-              }
-              cnt[rb] += __popc(gm);
-            }
+            const f32x4_t x = acc[rb][cb];
+            float s = w[rb][0] * fmaxf(x[0], 0.f);
+            s = fmaf(w[rb][1], fmaxf(x[1], 0.f), s);
+            s = fmaf(w[rb][2], fmaxf(x[2], 0.f), s);
+            sc[rb][cb] = fmaf(w[rb][3], fmaxf(x[3], 0.f), s);
           }
         }
-      }
-
-      if (pt0 + kPT < tp) {
-        bool fenced = false;
+        // causal pool mask, only on tiles some query of the wave sees in part
+        if (pt0 + kPT > ncmin) {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          uint64_t need = ballot(cnt[rb] > cap - kPT);
-          if (need && !fenced) {
-            __threadfence_block();  // this wave's candidate stores are visible
-            fenced = true;
+          for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+              if (pt0 + 16 * cb + c16 >= nc[rb]) sc[rb][cb] = NEG_INF;
+        }
+        // survivors: score strictly above the query's running threshold
+        uint64_t M[4][4];
+        uint64_t any = 0;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            M[rb][cb] = ballot(sc[rb][cb] > tau[rb]);
+            any |= M[rb][cb];
           }
-          while (need) {
-            const int L = __ffsll((long long)need) - 1;
-            const int gq = L >> 4;
-            need &= ~(0xFFFFull << (16 * gq));
-            const int n = __shfl(cnt[rb], L, kWave);
-            const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
-            const float T = select_and_compact(a.cand + base, n, topk, hist, nullptr);
-            if (g == gq) {
-              cnt[rb] = topk;
-              tau[rb] = T;
+        if (any) {
+          // append in pool order: per row block, column blocks ascending
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              if (M[rb][cb]) {
+                const uint32_t gm = (uint32_t)(M[rb][cb] >> (16 * g)) & 0xFFFFu;
+                if ((gm >> c16) & 1u) {
+                  const int slot = __popc(gm & lane_below) + cnt[rb];
+                  u32x2_t e;
+                  e[0] = order_key(sc[rb][cb] + 0.f);  // -0 -> +0
+                  e[1] = (uint32_t)(pt0 + 16 * cb + c16);
+                  clist[rb][slot] = e;
+                }
+                cnt[rb] += __popc(gm);
+              }
             }
           }
         }
+
+        // a list that could overflow during the next tile keeps its top-klim
+        if (i + 1 < nt) {
+          bool fenced = false;
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            uint64_t need = ballot(cnt[rb] > cap - kPT);
+            if (need && !fenced) {
+              __threadfence_block();  // this wave's candidate stores are visible
+              fenced = true;
+            }
+            while (need) {
+              const int L = __ffsll((long long)need) - 1;
+              const int gq = L >> 4;
+              need &= ~(0xFFFFull << (16 * gq));
+              const int n = __shfl(cnt[rb], L, kWave);
+              const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
+              const float T = select_and_compact(a.cand + base, n, klim, hist, nullptr);
+              if (g == gq) {
+                cnt[rb] = klim;
+                tau[rb] = T;
+              }
+            }
+          }
+        }
+        lds_barrier();
       }
-      lds_barrier();
+    };
+
+    if (kTwoPhase) {
+      const int r = a.sample_rank;
+      stream(0, a.sample_stride, r);
+      // threshold of phase 2: the r-th best sampled score (-inf if fewer)
+      __threadfence_block();
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = __shfl(cnt[rb], 16 * gq, kWave);
+          float T = NEG_INF;
+          if (n >= r) {
+            const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
+            T = select_and_compact(a.cand + base, n, r, hist, nullptr);
+          }
+          if (g == gq) {
+            tau[rb] = float_below(T);
+            cnt[rb] = 0;
+          }
+        }
+      }
     }
+    stream(0, 1, topk);
 
     // final selection, written straight to the output rows
     __threadfence_block();
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       for (int gq = 0; gq < 4; ++gq) {
-        const int64_t qr = q0 + 16 * wave + 4 * rb + gq;
-        if (qr >= a.Sq) continue;
+        const int64_t qr = row_of(q0 + 16 * wave + 4 * rb + gq);
+        if (qr < 0) continue;
         const int n = __shfl(cnt[rb], 16 * gq, kWave);
+        const int need = min(topk, __shfl(nc[rb], 16 * gq, kWave));
+        if (kTwoPhase && n < need) {  // threshold estimate too high
+          if (lane == 0) a.fb_rows[atomicAdd(a.fb_count, 1u)] = (int32_t)qr;
+          continue;
+        }
         const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
         int32_t* dst = a.idx_out + qr * topk;
         int filled = n;
@@ -468,7 +530,7 @@ int resident_index_blocks() {
   if (cache[dev] == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, indexer_topk_kernel, kThreads, 0) !=
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, indexer_topk_kernel<true>, kThreads, 0) !=
             hipSuccess ||
         cus * per <= 0) {
       (void)hipGetLastError();
@@ -481,16 +543,31 @@ int resident_index_blocks() {
 
 }  // namespace
 
+// Phase-1 sample: every kSampleStride-th pool tile.  The r-th best sampled
+// score t has about kSampleStride * r pools of the full range at or above it,
+// with a spread of about kSampleStride * sqrt(r); r is the smallest value with
+// kSampleStride * (r - 3 sqrt(r)) >= k, three spreads of margin before a query
+// needs the exact pass.
+constexpr int kSampleStride = 16;
+
+int sample_rank(int topk) {
+  const double x = (3.0 + std::sqrt(9.0 + 4.0 * topk / kSampleStride)) / 2.0;
+  const int r = (int)std::ceil(x * x);
+  return r < topk ? r : topk;
+}
+
 hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   const IndexWorkspace L = index_ws_layout(ia.Sq, ia.Sk, ia.topk);
   char* ws = static_cast<char*>(ia.ws);
   uint16_t* kpool = reinterpret_cast<uint16_t*>(ws + L.kpool_off);
+  uint32_t* fb_count = reinterpret_cast<uint32_t*>(ws + L.fb_off);
+  int32_t* fb_rows = reinterpret_cast<int32_t*>(ws + L.fb_off + 256);
   const int64_t n_pools = ia.Sk / 4;
   const int64_t n_padded = index_padded_pools(ia.Sk);
   {
     const int64_t threads = n_padded * 8;
     pool_keys_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(
-        ia.k_idx, kpool, n_pools, n_padded);
+        ia.k_idx, kpool, n_pools, n_padded, fb_count);
   }
   KernelArgs a;
   a.q_idx = ia.q_idx;
@@ -503,13 +580,20 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   a.heads = ia.heads;
   a.topk = ia.topk;
   a.cap = index_candidate_cap(ia.topk);
-  a.ntiles = (ia.Sq + kQT - 1) / kQT;
+  a.sample_stride = kSampleStride;
+  a.sample_rank = sample_rank(ia.topk);
+  a.rows = fb_rows;
+  a.nrows = fb_count;
+  a.fb_count = fb_count;
+  a.fb_rows = fb_rows;
   a.cand = reinterpret_cast<u32x2_t*>(ws + L.cand_off);
   a.idx_out = ia.idx_out;
   int64_t slots = index_slots(ia.Sq);  // the workspace holds candidate lists for this many
   const int64_t resident = resident_index_blocks();
   if (resident < slots) slots = resident;
-  indexer_topk_kernel<<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
+  indexer_topk_kernel<true><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
+  // queries whose threshold estimate was too high, scored exactly
+  indexer_topk_kernel<false><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
