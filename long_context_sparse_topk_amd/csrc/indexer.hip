@@ -107,7 +107,9 @@ __device__ __forceinline__ void load_chunk(const u32x2_t* __restrict__ list, int
   }
 }
 
-__device__ float select_and_compact(u32x2_t* __restrict__ list, int n, int k, uint32_t* hist,
+// Steps of a chunk are skipped (wave-uniformly) past the list end, so short
+// lists cost in proportion to their length.
+__device__ __forceinline__ float select_and_compact(u32x2_t* __restrict__ list, int n, int k, uint32_t* hist,
                                     int32_t* __restrict__ out) {
   const int lane = lane_id();
   const int nch = (n + kChunk - 1) / kChunk;
@@ -119,6 +121,7 @@ __device__ float select_and_compact(u32x2_t* __restrict__ list, int n, int k, ui
     if (nch > 1) load_chunk(list, c * kChunk, n, e);
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
+      if (c * kChunk + i * kWave >= n) break;
       if (c * kChunk + i * kWave + lane < n) {
         o |= e[i][0];
         an &= e[i][0];
@@ -149,6 +152,7 @@ __device__ float select_and_compact(u32x2_t* __restrict__ list, int n, int k, ui
         if (nch > 1) load_chunk(list, c * kChunk, n, e);
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
+          if (c * kChunk + i * kWave >= n) break;
           const bool in = c * kChunk + i * kWave + lane < n;
           if (in && (e[i][0] & hmask) == want) atomicAdd(&hist[(e[i][0] >> shift) & dmask], 1u);
         }
@@ -189,6 +193,7 @@ __device__ float select_and_compact(u32x2_t* __restrict__ list, int n, int k, ui
     if (nch > 1) load_chunk(list, c * kChunk, n, e);
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
+      if (c * kChunk + i * kWave >= n) break;
       const bool in = c * kChunk + i * kWave + lane < n;
       const bool gtf = in && e[i][0] > T;
       const bool eqf = in && e[i][0] == T;
@@ -222,8 +227,6 @@ struct KernelArgs {
   int64_t Sq, Sk;
   int n_pools;
   int heads, topk, cap;
-  int sample_stride;       // phase 1 streams every sample_stride-th pool tile
-  int sample_rank;         // r: phase 1 keeps the r-th best sampled score
   const int32_t* rows;     // exact pass: rows to score (the fallback list)
   const uint32_t* nrows;   // exact pass: device count of rows
   uint32_t* fb_count;      // two-phase pass: fallback list length
@@ -231,6 +234,15 @@ struct KernelArgs {
   u32x2_t* cand;           // [slots][kQT][cap] (order key, pool id)
   int32_t* idx_out;
 };
+
+// Phase-1 sample: every kSampleStride-th pool tile.  With a fraction f of a
+// query's causal pools sampled, about r/f pools score at or above the r-th
+// best sampled score, with a spread of about sqrt(r)/f; r is the smallest
+// value with r - kSampleZ sqrt(r) >= k f, kSampleZ spreads of margin before
+// the query needs the exact pass.
+constexpr int kSampleStride = 16;
+constexpr float kSampleZ = 5.f;
+constexpr int kSampleKeep = 8;   // sampled scores kept per lane and query
 
 // largest float below x (x finite or -inf); +0 and -0 are one score
 __device__ __forceinline__ float float_below(float x) {
@@ -343,11 +355,12 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       }
     };
 
-    // Stream pool tiles first, first+step, ... < ntp, keeping each query's
-    // running top-klim.  Tile 0 of a stream is always loaded (in bounds: the
-    // keys are padded to >= 1 tile) so every path into the loop has waited
-    // for the A operands.
-    auto stream = [&](int first, int step, int klim) {
+    // Stream pool tiles first, first+step, ... < ntp; `consume(sc, pt0, more)`
+    // receives each tile's scores (-inf where a pool is not causal for the
+    // query).  Tile 0 of a stream is always loaded (in bounds: the keys are
+    // padded to >= 1 tile) so every path into the loop has waited for the A
+    // operands.
+    auto stream = [&](int first, int step, auto&& consume) {
       const int nt = first < ntp ? (ntp - first + step - 1) / step : 0;
       gload(first < ntp ? first : 0);
       lstore(lds_k[0]);
@@ -395,87 +408,133 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
             for (int cb = 0; cb < 4; ++cb)
               if (pt0 + 16 * cb + c16 >= nc[rb]) sc[rb][cb] = NEG_INF;
         }
-        // survivors: score strictly above the query's running threshold
-        uint64_t M[4][4];
-        uint64_t any = 0;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            M[rb][cb] = ballot(sc[rb][cb] > tau[rb]);
-            any |= M[rb][cb];
-          }
-        if (any) {
-          // append in pool order: per row block, column blocks ascending
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-              if (M[rb][cb]) {
-                const uint32_t gm = (uint32_t)(M[rb][cb] >> (16 * g)) & 0xFFFFu;
-                if ((gm >> c16) & 1u) {
-                  const int slot = __popc(gm & lane_below) + cnt[rb];
-                  u32x2_t e;
-                  e[0] = order_key(sc[rb][cb] + 0.f);  // -0 -> +0
-                  e[1] = (uint32_t)(pt0 + 16 * cb + c16);
-                  clist[rb][slot] = e;
-                }
-                cnt[rb] += __popc(gm);
-              }
-            }
-          }
-        }
-
-        // a list that could overflow during the next tile keeps its top-klim
-        if (i + 1 < nt) {
-          bool fenced = false;
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            uint64_t need = ballot(cnt[rb] > cap - kPT);
-            if (need && !fenced) {
-              __threadfence_block();  // this wave's candidate stores are visible
-              fenced = true;
-            }
-            while (need) {
-              const int L = __ffsll((long long)need) - 1;
-              const int gq = L >> 4;
-              need &= ~(0xFFFFull << (16 * gq));
-              const int n = __shfl(cnt[rb], L, kWave);
-              const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
-              const float T = select_and_compact(a.cand + base, n, klim, hist, nullptr);
-              if (g == gq) {
-                cnt[rb] = klim;
-                tau[rb] = T;
-              }
-            }
-          }
-        }
+        consume(sc, pt0, i + 1 < nt);
         lds_barrier();
       }
     };
 
     if (kTwoPhase) {
-      const int r = a.sample_rank;
-      stream(0, a.sample_stride, r);
-      // threshold of phase 2: the r-th best sampled score (-inf if fewer)
-      __threadfence_block();
+      // Phase 1: each lane keeps, per query, the 8 best sampled scores of
+      // its pool column (descending, in registers).  Their union holds at
+      // most every sampled score, so its r-th best is at most the sample's.
+      int rq[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = __shfl(cnt[rb], 16 * gq, kWave);
-          float T = NEG_INF;
-          if (n >= r) {
-            const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
-            T = select_and_compact(a.cand + base, n, r, hist, nullptr);
+        // r from the fraction f of the query's causal pools the sample
+        // covers; 0 = no estimate (threshold stays -inf)
+        const int n_full = nc[rb] / kPT, part = nc[rb] % kPT;
+        const int s_q = kPT * ((n_full + kSampleStride - 1) / kSampleStride) +
+                        (n_full % kSampleStride == 0 ? part : 0);
+        int r = 0;
+        if (nc[rb] > topk && s_q > 0) {
+          const float f = (float)s_q / (float)nc[rb];
+          const float x = 0.5f * (kSampleZ + sqrtf(kSampleZ * kSampleZ + 4.f * topk * f));
+          r = (int)ceilf(x * x);
+          if (r >= s_q || r > kSampleKeep * 16 * 3 / 4) r = 0;
+        }
+        rq[rb] = r;
+      }
+      float best[4][kSampleKeep];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int j = 0; j < kSampleKeep; ++j) best[rb][j] = NEG_INF;
+      stream(0, kSampleStride, [&](float (&sc)[4][4], int, bool) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            float x = sc[rb][cb];
+            if (ballot(x > best[rb][kSampleKeep - 1])) {
+#pragma unroll
+              for (int j = 0; j < kSampleKeep; ++j) {
+                const float hi = fmaxf(best[rb][j], x);
+                x = fminf(best[rb][j], x);
+                best[rb][j] = hi;
+              }
+            }
           }
-          if (g == gq) {
-            tau[rb] = float_below(T);
-            cnt[rb] = 0;
+        }
+      });
+      // r-th best of the 16 lanes x kSampleKeep kept scores of each query:
+      // the largest key v with at least r kept keys >= v, bit by bit
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        uint32_t kk[kSampleKeep];
+#pragma unroll
+        for (int j = 0; j < kSampleKeep; ++j) kk[j] = order_key(best[rb][j] + 0.f);
+        uint32_t pre_k = 0u;
+        for (int b = 31; b >= 0; --b) {
+          const uint32_t cand_k = pre_k | (1u << b);
+          int c = 0;
+#pragma unroll
+          for (int j = 0; j < kSampleKeep; ++j) c += kk[j] >= cand_k ? 1 : 0;
+          c += __shfl_xor(c, 1, kWave);
+          c += __shfl_xor(c, 2, kWave);
+          c += __shfl_xor(c, 4, kWave);
+          c += __shfl_xor(c, 8, kWave);
+          if (c >= rq[rb]) pre_k = cand_k;
+        }
+        tau[rb] = rq[rb] > 0 ? float_below(key_to_float(pre_k)) : NEG_INF;
+      }
+    }
+
+    // Phase 2 (or the exact pass): every tile; survivors of the running
+    // threshold are appended to the query's list in pool order, and a list
+    // that could overflow during the next tile keeps its top-k.
+    stream(0, 1, [&](float (&sc)[4][4], int pt0, bool more) {
+      uint64_t M[4][4];
+      uint64_t any = 0;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          M[rb][cb] = ballot(sc[rb][cb] > tau[rb]);
+          any |= M[rb][cb];
+        }
+      if (any) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            if (M[rb][cb]) {
+              const uint32_t gm = (uint32_t)(M[rb][cb] >> (16 * g)) & 0xFFFFu;
+              if ((gm >> c16) & 1u) {
+                const int slot = __popc(gm & lane_below) + cnt[rb];
+                u32x2_t e;
+                e[0] = order_key(sc[rb][cb] + 0.f);  // -0 -> +0
+                e[1] = (uint32_t)(pt0 + 16 * cb + c16);
+                clist[rb][slot] = e;
+              }
+              cnt[rb] += __popc(gm);
+            }
           }
         }
       }
-    }
-    stream(0, 1, topk);
+      if (more) {
+        bool fenced = false;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          uint64_t need = ballot(cnt[rb] > cap - kPT);
+          if (need && !fenced) {
+            __threadfence_block();  // this wave's candidate stores are visible
+            fenced = true;
+          }
+          while (need) {
+            const int L = __ffsll((long long)need) - 1;
+            const int gq = L >> 4;
+            need &= ~(0xFFFFull << (16 * gq));
+            const int n = __shfl(cnt[rb], L, kWave);
+            const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
+            const float T = select_and_compact(a.cand + base, n, topk, hist, nullptr);
+            if (g == gq) {
+              cnt[rb] = topk;
+              tau[rb] = T;
+            }
+          }
+        }
+      }
+    });
 
     // final selection, written straight to the output rows
     __threadfence_block();
@@ -543,19 +602,6 @@ int resident_index_blocks() {
 
 }  // namespace
 
-// Phase-1 sample: every kSampleStride-th pool tile.  The r-th best sampled
-// score t has about kSampleStride * r pools of the full range at or above it,
-// with a spread of about kSampleStride * sqrt(r); r is the smallest value with
-// kSampleStride * (r - 3 sqrt(r)) >= k, three spreads of margin before a query
-// needs the exact pass.
-constexpr int kSampleStride = 16;
-
-int sample_rank(int topk) {
-  const double x = (3.0 + std::sqrt(9.0 + 4.0 * topk / kSampleStride)) / 2.0;
-  const int r = (int)std::ceil(x * x);
-  return r < topk ? r : topk;
-}
-
 hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   const IndexWorkspace L = index_ws_layout(ia.Sq, ia.Sk, ia.topk);
   char* ws = static_cast<char*>(ia.ws);
@@ -580,8 +626,6 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   a.heads = ia.heads;
   a.topk = ia.topk;
   a.cap = index_candidate_cap(ia.topk);
-  a.sample_stride = kSampleStride;
-  a.sample_rank = sample_rank(ia.topk);
   a.rows = fb_rows;
   a.nrows = fb_count;
   a.fb_count = fb_count;
