@@ -31,7 +31,7 @@ import synthetic as syn  # noqa: E402
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 BF16_PEAK = 2.5e15         # flop/s, dense bf16 MFMA
 SCALE = 1.0 / np.sqrt(128.0)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "attn_fwd_kernel": "long_context_sparse_topk_amd/csrc/attn_fwd.hip",
     "indexer_topk_kernel": "long_context_sparse_topk_amd/csrc/indexer.hip",

@@ -102,9 +102,12 @@ const char* dsa_last_error(void);
  *
  * Supported: idx_dim == 64, 1 <= idx_heads <= 4, pool == 4,
  * 1 <= topk <= 2048, q_chunk >= 1, 1 <= Sq, 1 <= Sk < 2^31.
- * q_chunk is the query chunk: the queries that share one pass over the pool
- * keys.  The kernel scores chunks in sub-tiles of 64 queries; the result
- * does not depend on q_chunk.
+ * q_chunk is the query chunk of the pages' indexer, there a bound on the
+ * memory of materialised score rows.  No score row leaves the chip here, so
+ * the chunk bounds nothing: it is validated (>= 1) and otherwise unused; the
+ * kernel scores sub-tiles of 64 queries and the result does not depend on
+ * q_chunk.  The workspace (see dsa_index_topk_ws_bytes) holds the pooled
+ * keys and fixed-size candidate lists for at most 512 workgroups.
  */
 size_t dsa_index_topk_ws_bytes(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim,
                                int32_t pool, int32_t topk, int32_t q_chunk);

@@ -10,7 +10,7 @@ namespace dsa {
 // ---- indexer + top-k -------------------------------------------------------
 constexpr int kIndexQueryTile = 64;     // queries per workgroup sub-tile
 constexpr int kIndexPoolTile = 64;      // pools per LDS-staged key tile
-constexpr int kIndexMaxSlots = 1024;    // resident workgroups owning candidate buffers
+constexpr int kIndexMaxSlots = 512;     // workgroups owning candidate lists (2 per CU x 256 CUs)
 constexpr int kMaxTopk = 2048;
 
 // per-query candidate capacity (multiple of 64, >= topk + one pool tile):
