@@ -13,11 +13,19 @@ constexpr int kIndexPoolTile = 64;      // pools per LDS-staged key tile
 constexpr int kIndexMaxSlots = 512;     // workgroups owning candidate lists (2 per CU x 256 CUs)
 constexpr int kMaxTopk = 2048;
 
-// per-query candidate capacity (multiple of 64, >= topk + one pool tile):
-// each compaction absorbs about 2*topk survivors
+// Survivors of the running threshold are staged in LDS per (wave, row block
+// of 4 queries) and moved to the per-query lists in HBM when a stage is
+// within one pool tile's worst case (4 queries x 64 pools) of its end, and
+// at a fixed period.
+constexpr int kIndexStage = 440;
+
+// per-query candidate capacity (multiple of 64): a list is compacted to topk
+// entries when a flush leaves it within one stage of the end, so each
+// compaction absorbs about 2*topk survivors
 inline int index_candidate_cap(int topk) {
   int c = 3 * topk;
-  if (c < topk + kIndexPoolTile) c = topk + kIndexPoolTile;
+  if (c < topk + 384) c = topk + 384;
+  c += kIndexStage;
   return (c + 63) / 64 * 64;
 }
 

@@ -12,15 +12,16 @@
 //                       query x indexer-head), stream the causal pool range in
 //                       tiles of 64 pools staged in LDS; bf16 MFMA 16x16x32 gives
 //                       the 4 head dot products of a (query, pool) pair in one
-//                       lane, so ReLU, the head weights and the head sum are an
-//                       in-register epilogue.  Each score is compared with the
-//                       query's running threshold (the k-th best key so far);
-//                       survivors are appended, in pool order, to the query's
-//                       candidate list in the workspace.  When a list could
-//                       overflow, the owning wave selects its exact top-k with a
-//                       radix select over the order-preserving float keys and
-//                       compacts it stably, raising the threshold.  The final
-//                       list is already ascending in pool id.
+//                       lane (head weights folded into the query operand), so
+//                       the weighted ReLU and the head sum are an in-register
+//                       epilogue.  Each score is compared with the query's
+//                       running threshold; survivors are staged in LDS and
+//                       moved, in pool order, to the query's candidate list in
+//                       the workspace.  When a list could overflow, the owning
+//                       wave selects its exact top-k with a radix select over
+//                       the order-preserving float keys and compacts it
+//                       stably, raising the threshold.  The final list is
+//                       already ascending in pool id.
 //
 // Exactness: pools are streamed in ascending id order and a candidate joins the
 // list only if its score is strictly greater than the threshold score, so an
@@ -43,6 +44,9 @@ constexpr int kPT = kIndexPoolTile;  // 64 pools per staged tile
 constexpr int kWaves = 4;            // 16 queries per wave
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer: 32-bit data format, no swizzle
+constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
+constexpr int kWaitVmcnt2 = 0x0F72;        // s_waitcnt vmcnt(2) expcnt(7) lgkmcnt(15)
+constexpr int kRing = 3;                   // LDS key-tile buffers
 
 // ---------------------------------------------------------------------------
 
@@ -209,6 +213,10 @@ __device__ __forceinline__ float select_and_compact(u32x2_t* __restrict__ list, 
       eqseen += __popcll(EQ);
     }
   }
+  // Chunk loads past the list end are never consumed; wait for them here so
+  // that the callers' loops do not inherit outstanding loads (which would
+  // make every later wait on the key prefetch a full vmcnt(0)).
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   return key_to_float(T);
 }
 
@@ -244,11 +252,25 @@ constexpr int kSampleStride = 16;
 constexpr float kSampleZ = 5.f;
 constexpr int kSampleKeep = 8;   // sampled scores kept per lane and query
 
+constexpr int kStage = kIndexStage;
+constexpr int kFlushPeriod = 32;                 // tiles between periodic stage flushes
+constexpr uint32_t kTagShift = 30;               // staged pool id: query (0..3) in bits 30-31
+constexpr uint32_t kPoolMask = (1u << kTagShift) - 1u;
+
 // largest float below x (x finite or -inf); +0 and -0 are one score
 __device__ __forceinline__ float float_below(float x) {
   if (x == 0.f) return -__builtin_bit_cast(float, 1u);
   if (x == -__builtin_huge_valf()) return x;
   return key_to_float(order_key(x) - 1u);
+}
+
+// 8 bf16 query values times the head weight, rounded back to bf16
+__device__ __forceinline__ bf16x8_t fold_weight(u32x4_t q, float w) {
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = cvt_pk_bf16(bf16_to_f32(q[j] & 0xFFFFu) * w, bf16_to_f32(q[j] >> 16) * w);
+  return as_bf16x8(o);
 }
 
 // Two-phase pass (kTwoPhase): per query, phase 1 streams a strided sample of
@@ -258,10 +280,23 @@ __device__ __forceinline__ float float_below(float x) {
 // score is >= the k-th best score >= t), so the result is exact; otherwise
 // the query goes to the fallback list, which the exact pass (!kTwoPhase:
 // one phase, threshold from -inf) then scores.
+//
+// Scores: the head weight is folded into the query operand, bf16(w_h q_h),
+// so w_h ReLU(q_h . k) = clamp_h(bf16(w_h q_h) . k) with clamp_h = max(., 0)
+// for w_h >= 0 and min(., 0) for w_h < 0, one v_med3 against (+-inf, 0).
+// For the integer indexer inputs every product and sum is exact.
+//
+// Survivors of the running threshold go to a per-(wave, row block) stage in
+// LDS: one wave-uniform count and mbcnt give the slot, and the pool id
+// carries the query (0..3) of the row block in its top bits.  Before the next
+// key prefetch is issued, a stage holding 64 or more entries is moved to the
+// per-query lists in HBM (stable per query, so each list stays in pool
+// order).  Keeping global stores out of the scoring loop keeps the prefetch
+// wait exact (loads and stores share one completion counter).
 template <bool kTwoPhase>
 __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a) {
-  __shared__ __align__(16) u32x4_t lds_k[2][kPT * 8];       // 2 x (64 pools x 128 B), swizzled
-  __shared__ uint32_t lds_hist[kWaves][256];
+  __shared__ __align__(16) u32x4_t lds_k[kRing][kPT * 8];   // ring of (64 pools x 128 B), swizzled
+  __shared__ uint32_t lds_st[kWaves][4][2][kStage];  // stage: [0] score bits, [1] (query tag, pool id)
   __shared__ int lds_np[kWaves];
 
   const int tid = threadIdx.x;
@@ -271,10 +306,17 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
   const int c16 = lane & 15;
   const int cap = a.cap;
   const int topk = a.topk;
-  uint32_t* hist = lds_hist[wave];
   const float NEG_INF = -__builtin_huge_valf();
+  const float POS_INF = __builtin_huge_valf();
   const int64_t nrow = kTwoPhase ? a.Sq : (int64_t)__builtin_amdgcn_readfirstlane(*a.nrows);
   const int64_t ntiles = (nrow + kQT - 1) / kQT;
+  const uint32_t lane_tag = ((uint32_t)g << kTagShift) | (uint32_t)c16;
+  int dma_off[2];  // byte offset in a key tile of the chunk this thread's loads bring
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = tid + kThreads * j, pr = p >> 3;
+    dma_off[j] = (pr * 8 + ((p & 7) ^ (pr & 7))) * 16;
+  }
 
   for (int64_t it = 0;; ++it) {
     const int64_t rank = snake_rank(it, blockIdx.x, gridDim.x);
@@ -285,9 +327,11 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       return kTwoPhase ? i : (int64_t)a.rows[i];
     };
 
-    // A operands: row (4*qq + h) of row block rb -> query 16*wave + 4*rb + qq, head h
+    // A operands: row (4*qq + h) of row block rb -> query 16*wave + 4*rb + qq,
+    // head h, weight folded in.  cl[rb][h]: the clamp side of the lane's query
+    // (row block rb, query g) and head h.
     bf16x8_t A[4][2];
-    float w[4][4];
+    float cl[4][4];
     int nc[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -296,8 +340,11 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         const int h = c16 & 3;
         const bool ok = qr >= 0 && h < a.heads;
         const uint16_t* src = a.q_idx + (qr * a.heads + h) * kDI + 8 * g;
+        const float wv = ok ? bf16_to_f32(a.w_idx[qr * a.heads + h]) : 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) A[rb][ks] = ok ? load_bf16x8(src + 32 * ks) : zero_bf16x8();
+        for (int ks = 0; ks < 2; ++ks)
+          A[rb][ks] = ok ? fold_weight(*reinterpret_cast<const u32x4_t*>(src + 32 * ks), wv)
+                         : zero_bf16x8();
       }
       {
         const int64_t qr = row_of(q0 + 16 * wave + 4 * rb + g);
@@ -309,8 +356,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         }
         nc[rb] = ok ? (int)((pos + 1) >> 2) : 0;
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-          w[rb][h] = (ok && h < a.heads) ? bf16_to_f32(a.w_idx[qr * a.heads + h]) : 0.f;
+        for (int h = 0; h < 4; ++h) {
+          const float wv = (ok && h < a.heads) ? bf16_to_f32(a.w_idx[qr * a.heads + h]) : 0.f;
+          cl[rb][h] = wv < 0.f ? NEG_INF : POS_INF;
+        }
       }
     }
     int ncm = max(max(nc[0], nc[1]), max(nc[2], nc[3]));
@@ -325,54 +374,51 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     const int tp = max(max(lds_np[0], lds_np[1]), max(lds_np[2], lds_np[3]));
     const int ntp = (tp + kPT - 1) / kPT;   // pool tiles in the tile's causal range
 
-    int cnt[4] = {0, 0, 0, 0};
     float tau[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
     const int64_t wbase = ((int64_t)blockIdx.x * kQT + 16 * wave) * cap;
-    // this lane's query list of each row block: (order key, pool id) pairs
-    u32x2_t* clist[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) clist[rb] = a.cand + wbase + (int64_t)(4 * rb + g) * cap;
-    const uint32_t lane_below = (1u << c16) - 1u;
 
-    // pool-key tiles: global -> registers two tiles ahead, registers -> LDS
-    // one tile ahead (double buffer), one LDS-only barrier per tile.  The
-    // loads are unconditional raw buffer loads (the keys are padded to whole
-    // tiles) from a per-tile resource and a loop-invariant per-thread offset.
-    u32x4_t pre[2];
-    auto gload = [&](int tile) {
+    // Pool-key tiles go straight from HBM to LDS (buffer loads with the LDS
+    // destination) through a ring of kRing buffers, two tiles ahead of the
+    // one being scored.  Lane l of a load instruction writes LDS chunk
+    // (base + l); its source offset is chosen so that LDS row pr, chunk ch
+    // holds key chunk ch ^ (pr & 7) (the swizzle that spreads the B-operand
+    // reads over the banks).  The loads are unconditional (the keys are
+    // padded to whole tiles) from a per-tile resource and loop-invariant
+    // per-thread offsets.
+    auto dma = [&](int tile, int buf) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a.kpool + (int64_t)tile * kPT * kDI), (short)0, kPT * kDI * 2, kBufferWord3);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (tid + kThreads * j) * 16, 0, 0);
-    };
-    auto lstore = [&](u32x4_t* buf) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = tid + kThreads * j;
-        const int pr = c >> 3, ch = c & 7;
-        buf[pr * 8 + (ch ^ (pr & 7))] = pre[j];
-      }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)&lds_k[buf][kThreads * j + kWave * wave], 16,
+            dma_off[j], 0, 0, 0);
     };
 
-    // Stream pool tiles first, first+step, ... < ntp; `consume(sc, pt0, more)`
-    // receives each tile's scores (-inf where a pool is not causal for the
-    // query).  Tile 0 of a stream is always loaded (in bounds: the keys are
-    // padded to >= 1 tile) so every path into the loop has waited for the A
-    // operands.
-    auto stream = [&](int first, int step, auto&& consume) {
+    // Stream pool tiles first, first+step, ... < ntp.  Per tile i: wait for
+    // this thread's part of tile i and meet at the barrier (tile i is then in
+    // LDS and every wave is done with tile i-1's buffer), run
+    // `before_load(i)` (it may issue global stores), start tile i+2, and
+    // hand the tile's scores to `consume(sc, pt0)` (-inf where a pool is not
+    // causal for the query).  Loads complete in order among themselves, so
+    // with tile i+1's two loads younger than tile i's, "at most 2
+    // outstanding" means tile i has landed, whatever the stores do.  Tile 0
+    // of a stream is always loaded (in bounds: the keys are padded to >= 1
+    // tile).
+    auto stream = [&](int first, int step, auto&& before_load, auto&& consume) {
       const int nt = first < ntp ? (ntp - first + step - 1) / step : 0;
-      gload(first < ntp ? first : 0);
-      lstore(lds_k[0]);
-      if (nt > 1) gload(first + step);
-      lds_barrier();
+      dma(first < ntp ? first : 0, 0);
+      if (nt > 1) dma(first + step, 1);
+      int buf = 0;
       for (int i = 0; i < nt; ++i) {
         const int pt0 = (first + i * step) * kPT;
-        const u32x4_t* kb = lds_k[i & 1];
-        if (i + 1 < nt) {
-          lstore(lds_k[(i + 1) & 1]);
-          if (i + 2 < nt) gload(first + (i + 2) * step);
-        }
+        if (i + 1 < nt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt2);
+        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        lds_barrier();
+        const u32x4_t* kb = lds_k[buf];
+        before_load(i);
+        if (i + 2 < nt) dma(first + (i + 2) * step, buf == 0 ? 2 : buf - 1);
+        buf = buf == kRing - 1 ? 0 : buf + 1;
 
         // 16 output blocks of 16 (query x head) rows x 16 pools
         f32x4_t acc[4][4];
@@ -387,17 +433,18 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
             acc[rb][cb] = mfma32(A[rb][1], B1, mfma32(A[rb][0], B0, z));
           }
         }
-        // epilogue: ReLU, head weights, head sum (branch-free)
+        // epilogue: clamp each head to the side of its weight, sum the heads
         float sc[4][4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const f32x4_t x = acc[rb][cb];
-            float s = w[rb][0] * fmaxf(x[0], 0.f);
-            s = fmaf(w[rb][1], fmaxf(x[1], 0.f), s);
-            s = fmaf(w[rb][2], fmaxf(x[2], 0.f), s);
-            sc[rb][cb] = fmaf(w[rb][3], fmaxf(x[3], 0.f), s);
+            const float s01 = __builtin_amdgcn_fmed3f(x[0], cl[rb][0], 0.f) +
+                              __builtin_amdgcn_fmed3f(x[1], cl[rb][1], 0.f);
+            const float s23 = __builtin_amdgcn_fmed3f(x[2], cl[rb][2], 0.f) +
+                              __builtin_amdgcn_fmed3f(x[3], cl[rb][3], 0.f);
+            sc[rb][cb] = s01 + s23;
           }
         }
         // causal pool mask, only on tiles some query of the wave sees in part
@@ -408,9 +455,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
             for (int cb = 0; cb < 4; ++cb)
               if (pt0 + 16 * cb + c16 >= nc[rb]) sc[rb][cb] = NEG_INF;
         }
-        consume(sc, pt0, i + 1 < nt);
-        lds_barrier();
+        consume(sc, pt0);
       }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // a tile-0 load of an empty stream
+      lds_barrier();  // every wave is done with the ring before the next stream
     };
 
     if (kTwoPhase) {
@@ -439,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int j = 0; j < kSampleKeep; ++j) best[rb][j] = NEG_INF;
-      stream(0, kSampleStride, [&](float (&sc)[4][4], int, bool) {
+      stream(0, kSampleStride, [](int) {}, [&](float (&sc)[4][4], int) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
@@ -480,99 +528,168 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     }
 
     // Phase 2 (or the exact pass): every tile; survivors of the running
-    // threshold are appended to the query's list in pool order, and a list
-    // that could overflow during the next tile keeps its top-k.
-    stream(0, 1, [&](float (&sc)[4][4], int pt0, bool more) {
-      uint64_t M[4][4];
-      uint64_t any = 0;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          M[rb][cb] = ballot(sc[rb][cb] > tau[rb]);
-          any |= M[rb][cb];
-        }
-      if (any) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            if (M[rb][cb]) {
-              const uint32_t gm = (uint32_t)(M[rb][cb] >> (16 * g)) & 0xFFFFu;
-              if ((gm >> c16) & 1u) {
-                const int slot = __popc(gm & lane_below) + cnt[rb];
-                u32x2_t e;
-                e[0] = order_key(sc[rb][cb] + 0.f);  // -0 -> +0
-                e[1] = (uint32_t)(pt0 + 16 * cb + c16);
-                clist[rb][slot] = e;
-              }
-              cnt[rb] += __popc(gm);
-            }
-          }
-        }
-      }
-      if (more) {
-        bool fenced = false;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          uint64_t need = ballot(cnt[rb] > cap - kPT);
-          if (need && !fenced) {
-            __threadfence_block();  // this wave's candidate stores are visible
-            fenced = true;
-          }
-          while (need) {
-            const int L = __ffsll((long long)need) - 1;
-            const int gq = L >> 4;
-            need &= ~(0xFFFFull << (16 * gq));
-            const int n = __shfl(cnt[rb], L, kWave);
-            const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
-            const float T = select_and_compact(a.cand + base, n, topk, hist, nullptr);
-            if (g == gq) {
-              cnt[rb] = topk;
-              tau[rb] = T;
-            }
-          }
-        }
-      }
-    });
+    // threshold are staged, stages are flushed to the per-query lists, and a
+    // list that a flush leaves within one stage of its end keeps its top-k.
+    int nst[4] = {0, 0, 0, 0};   // staged entries per row block (wave-uniform)
+    int cnt_v = 0;               // lane q < 16: list length of wave query q = 4*rb + t
 
-    // final selection, written straight to the output rows
-    __threadfence_block();
+    // Entry j of stage rb (of n) is moved to the list of its query; `c` holds
+    // the 4 list lengths of the row block and advances (stable per query).
+    auto place = [&](int rb, int j0, int n, uint32_t fbits, uint32_t id, int (&c)[4]) {
+      const bool valid = j0 + lane < n;
+      const int t = (int)(id >> kTagShift);
+      int pos = 0;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      for (int gq = 0; gq < 4; ++gq) {
-        const int64_t qr = row_of(q0 + 16 * wave + 4 * rb + gq);
-        if (qr < 0) continue;
-        const int n = __shfl(cnt[rb], 16 * gq, kWave);
-        const int need = min(topk, __shfl(nc[rb], 16 * gq, kWave));
-        if (kTwoPhase && n < need) {  // threshold estimate too high
-          if (lane == 0) a.fb_rows[atomicAdd(a.fb_count, 1u)] = (int32_t)qr;
-          continue;
-        }
-        const int64_t base = wbase + (int64_t)(4 * rb + gq) * cap;
-        int32_t* dst = a.idx_out + qr * topk;
-        int filled = n;
-        if (n > topk) {
-          select_and_compact(a.cand + base, n, topk, hist, dst);
-          filled = topk;
-        } else {
-          const u32x2_t* src = a.cand + base;
-          for (int j0 = 0; j0 < n; j0 += 8 * kWave) {
-            int32_t v[8];
+      for (int tq = 0; tq < 4; ++tq) {
+        const bool mine = valid && t == tq;
+        const uint64_t Mt = ballot(mine);
+        if (mine) pos = c[tq] + mbcnt(Mt);
+        c[tq] += __popcll(Mt);
+      }
+      if (valid) {
+        u32x2_t e;
+        e[0] = order_key(__uint_as_float(fbits) + 0.f);  // -0 -> +0
+        e[1] = id & kPoolMask;
+        a.cand[wbase + (int64_t)(4 * rb + t) * cap + pos] = e;
+      }
+    };
+    // Move the stages flagged in fl to the lists.  The first 64 entries of
+    // every flagged stage are read before any is placed, so one LDS latency
+    // covers them all.
+    auto flush = [&](uint32_t fl) {
+      uint32_t f0[4], i0[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int j = j0 + i * kWave + lane;
-              v[i] = j < n ? (int32_t)src[j][1] : 0;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int j = j0 + i * kWave + lane;
-              if (j < n) dst[j] = v[i];
-            }
+      for (int rb = 0; rb < 4; ++rb) {
+        f0[rb] = 0u;
+        i0[rb] = 0u;
+        if ((fl >> rb) & 1u) {
+          if (lane < nst[rb]) {
+            f0[rb] = lds_st[wave][rb][0][lane];
+            i0[rb] = lds_st[wave][rb][1][lane];
           }
         }
-        for (int j = filled + lane; j < topk; j += kWave) dst[j] = -1;
       }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (!((fl >> rb) & 1u)) continue;
+        const int n = nst[rb];
+        int c[4];
+#pragma unroll
+        for (int tq = 0; tq < 4; ++tq) c[tq] = __builtin_amdgcn_readlane(cnt_v, 4 * rb + tq);
+        place(rb, 0, n, f0[rb], i0[rb], c);
+        for (int j0 = kWave; j0 < n; j0 += kWave) {
+          const int j = j0 + lane;
+          const uint32_t fb = j < n ? lds_st[wave][rb][0][j] : 0u;
+          const uint32_t id = j < n ? lds_st[wave][rb][1][j] : 0u;
+          place(rb, j0, n, fb, id, c);
+        }
+#pragma unroll
+        for (int tq = 0; tq < 4; ++tq) cnt_v = lane == 4 * rb + tq ? c[tq] : cnt_v;
+        nst[rb] = 0;
+      }
+    };
+
+    stream(0, 1,
+        [&](int i) {
+          // A flush costs about one store latency, whatever its size, and a
+          // wave that flushes holds up the others at the next barrier.  So
+          // all 4 stages of a wave are flushed together, when one of them
+          // could not take another tile's worth (4 x 64 entries), and every
+          // kFlushPeriod tiles (the same tiles in every wave).
+          bool full = false;
+          uint32_t fl = 0;
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            full |= nst[rb] > kStage - 4 * kWave;
+            fl |= nst[rb] > 0 ? 1u << rb : 0u;
+          }
+          if (!(full || (i > 0 && (i % kFlushPeriod) == 0)) || fl == 0) return;
+          flush(fl);
+          bool fenced = false;
+          for (uint32_t m = fl; m != 0; m &= m - 1) {
+            const int rb = __builtin_ctz(m);
+#pragma unroll 1
+            for (int tq = 0; tq < 4; ++tq) {
+              const int q = 4 * rb + tq;
+              const int n = __builtin_amdgcn_readlane(cnt_v, q);
+              if (n <= cap - kStage) continue;
+              if (!fenced) {
+                __threadfence_block();  // this wave's list stores are visible
+                fenced = true;
+              }
+              // the (just flushed, empty) stage of rb holds the histogram
+              const float T = select_and_compact(a.cand + wbase + (int64_t)q * cap, n, topk,
+                                                 lds_st[wave][rb][0], nullptr);
+              cnt_v = lane == q ? topk : cnt_v;
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (r == rb && g == tq) tau[r] = T;
+            }
+          }
+        },
+        [&](float (&sc)[4][4], int pt0) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              const bool keep = sc[rb][cb] > tau[rb];
+              const uint64_t M = ballot(keep);
+              if (M) {
+                if (keep) {
+                  const int slot = nst[rb] + mbcnt(M);
+                  uint32_t* st = &lds_st[wave][rb][0][slot];
+                  st[0] = __float_as_uint(sc[rb][cb]);
+                  st[kStage] = (uint32_t)(pt0 + 16 * cb) + lane_tag;
+                }
+                nst[rb] += __popcll(M);
+              }
+            }
+          }
+        });
+
+    // remaining stages, then the final selection written to the output rows
+    {
+      uint32_t fl = 0;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) fl |= nst[rb] > 0 ? 1u << rb : 0u;
+      if (fl) flush(fl);
+    }
+    __threadfence_block();
+#pragma unroll 1
+    for (int q = 0; q < 16; ++q) {
+      const int64_t qr = row_of(q0 + 16 * wave + q);
+      if (qr < 0) continue;
+      const int rb = q >> 2;
+      const int n = __builtin_amdgcn_readlane(cnt_v, q);
+      const int ncr = rb == 0 ? nc[0] : rb == 1 ? nc[1] : rb == 2 ? nc[2] : nc[3];
+      const int need = min(topk, __shfl(ncr, 16 * (q & 3), kWave));
+      if (kTwoPhase && n < need) {  // threshold estimate too high
+        if (lane == 0) a.fb_rows[atomicAdd(a.fb_count, 1u)] = (int32_t)qr;
+        continue;
+      }
+      const int64_t base = wbase + (int64_t)q * cap;
+      int32_t* dst = a.idx_out + qr * topk;
+      int filled = n;
+      if (n > topk) {
+        select_and_compact(a.cand + base, n, topk, lds_st[wave][0][0], dst);  // stages are empty
+        filled = topk;
+      } else {
+        const u32x2_t* src = a.cand + base;
+        for (int j0 = 0; j0 < n; j0 += 8 * kWave) {
+          int32_t v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int j = j0 + i * kWave + lane;
+            v[i] = j < n ? (int32_t)src[j][1] : 0;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int j = j0 + i * kWave + lane;
+            if (j < n) dst[j] = v[i];
+          }
+        }
+      }
+      for (int j = filled + lane; j < topk; j += kWave) dst[j] = -1;
     }
     lds_barrier();  // lds_np reuse in the next tile
   }
