@@ -35,7 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "attn_fwd_kernel": "long_context_sparse_topk_amd/csrc/attn_fwd.hip",
     "indexer_topk_kernel": "long_context_sparse_topk_amd/csrc/indexer.hip",
-    "attn_bwd_kernel": "long_context_sparse_topk_amd/csrc/attn_bwd.hip",
+    "sparse_attn_bwd": "long_context_sparse_topk_amd/csrc/attn_bwd.hip",   # dq + inverse lists + dk/dv
 }
 
 
@@ -59,14 +59,24 @@ def work(wl):
     nkeys = 4 * np.minimum(nc, wl.topk) + part
     H, k = wl.heads, wl.topk
     keys = int(nkeys.sum())
+    # (query row, pool) entries of the key sets: selected pools + own incomplete pool
+    entries = int((np.minimum(nc, wl.topk) + (part > 0)).sum())
+    n_pools = (wl.sk + 3) // 4
     per_q_fwd = 2 * H * 128 * 2 + 4 * H + 4 * k
-    per_q_bwd = 4 * H * 128 * 2 + 4 * H + 4 * k
+    # dq pass: q, o, dout read, dq written, lse, idx, the per-(row, head) record
+    per_q_dq = 4 * H * 128 * 2 + 4 * H + 4 * k + 16 * H
+    # dk/dv pass per entry: q and dout rows, the record, the list entry written and read
+    per_entry_kv = 2 * H * 128 * 2 + 16 * H + 8
     return {
         "index_flop": 512 * int(nc.sum()),          # 4 heads x 64 dims x 2 per (query, pool)
         "index_pairs": int(nc.sum()),
         "keys": keys,
+        "entries": entries,
         "fwd_bytes": 512 * keys + per_q_fwd * wl.sq,
-        "bwd_bytes": 1536 * keys + per_q_bwd * wl.sq,
+        # K, V rows gathered per key (dq pass); inverse lists (idx read twice);
+        # dk/dv pass entries; per pool K, V read and dK, dV written
+        "bwd_bytes": 512 * keys + per_q_dq * wl.sq + 8 * k * wl.sq + per_entry_kv * entries
+                     + 4 * 1024 * n_pools,
     }
 
 
@@ -95,7 +105,7 @@ class Layer:
             self.dq = torch.empty_like(self.out)
             self.dk = torch.empty((Sk, 128), dtype=torch.bfloat16, device=device)
             self.dv = torch.empty_like(self.dk)
-            self.ws_bwd = torch.empty(D.sparse_attn_bwd_ws_bytes(Sq, Sk, H), dtype=torch.uint8,
+            self.ws_bwd = torch.empty(D.sparse_attn_bwd_ws_bytes(Sq, Sk, H, k), dtype=torch.uint8,
                                       device=device)
         torch.cuda.synchronize()
 
@@ -240,7 +250,7 @@ def main():
                             "peak": HBM_PEAK / 1e9, "unit": "GB/s"},
     }
     if wl.backward:
-        kern["attn_bwd_kernel"] = {"s": avg["bwd"], "bound": "hbm",
+        kern["sparse_attn_bwd"] = {"s": avg["bwd"], "bound": "hbm",
                                    "achieved": w["bwd_bytes"] / avg["bwd"] / 1e9,
                                    "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     dom = max(kern, key=lambda n: kern[n]["s"])

@@ -89,9 +89,12 @@ const char* dsa_last_error(void);
  * idx_out[r, 0..m), m = min(topk, floor((i+1)/4)), then -1 to idx_out[r, m..topk).
  * Scores never reach device memory: the kernel keeps them on chip and only
  * streams candidate pool ids whose score beats a running per-query threshold.
- * Scoring is done in fp32 from bf16 products (bf16 pooled keys); for integer
- * indexer inputs in [-3, 3] every value is exact, so results equal the exact
- * real-number ranking.
+ * Scoring is done in fp32 from bf16 operands: the pooled keys are rounded to
+ * bf16 and each head weight is folded into its query as bf16(w * q), so that
+ * w * ReLU(q . k) is computed as a clamp of bf16(w * q) . k to the side of
+ * the weight's sign.  For integer indexer inputs in [-3, 3] every value is
+ * exact, so results equal the exact real-number ranking; for other inputs,
+ * scores carry those two bf16 roundings and near-ties may rank differently.
  *
  *   q_idx   [Sq, idx_heads, idx_dim] bf16   indexer queries
  *   k_idx   [Sk, idx_dim]            bf16   indexer keys (one per token)
@@ -147,20 +150,26 @@ int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32
  * Gradients of L = sum(dout * O) for the forward above, with
  *   P = exp(scale * q.k - lse),  Delta[r,h] = sum_d dout[r,h,d] * out[r,h,d],
  *   dS = P * (dout.v - Delta),
- *   dq[r,h] = scale * sum_j dS_j k[j]                     (written directly)
- *   dk[j]  += scale * sum_{r,h} dS q[r,h],  dv[j] += sum_{r,h} P dout[r,h]
- * dk/dv are accumulated in fp32 in the workspace with device atomics (their
- * summation order is therefore not fixed) and then rounded to bf16 into
- * dk/dv, which are overwritten; keys no query attends get 0.
+ *   dq[r,h] = scale * sum_j dS_j k[j]
+ *   dk[j]   = scale * sum_{r,h} dS q[r,h],  dv[j] = sum_{r,h} P dout[r,h]
+ * All sums are fp32; dq, dk and dv are rounded to bf16 (nearest even) and
+ * overwritten completely (0 for keys no row attends).  dq is computed per
+ * query row; dk and dv per pool of 4 keys, over the query rows whose key set
+ * holds the pool, found by inverting idx in the workspace.  The order in
+ * which a pool's rows are summed comes from device atomics and is not fixed.
  *
  *   q, out, dout [Sq, heads, head_dim] bf16   k, v [Sk, head_dim] bf16
  *   lse [Sq, heads] fp32 (from the forward)   idx, q_pos as in the forward
  *   dq [Sq, heads, head_dim] bf16             dk, dv [Sk, head_dim] bf16
  *   ws  workspace of ws_bytes >= dsa_sparse_attn_bwd_ws_bytes(...) bytes
+ *       (Delta, per-pool offsets and the inverted lists: about
+ *       4 * (Sq * (heads + topk + 1) + Sk / 4) bytes)
  *
- * Supported: as the forward.
+ * Supported: as the forward, and Sq * (topk + 1) < 2^31.  Returns 0 bytes
+ * for arguments outside that.
  */
-size_t dsa_sparse_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t heads, int32_t head_dim);
+size_t dsa_sparse_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t heads, int32_t head_dim,
+                                    int32_t topk);
 
 int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                         const void* dout, const float* lse, const int32_t* idx,

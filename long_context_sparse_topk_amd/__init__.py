@@ -41,7 +41,7 @@ SIGNATURES = {
                                       _P, _P, _SZ, _P]),
     "dsa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
                                            _F, _P, _P, _P]),
-    "dsa_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32]),
+    "dsa_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
     "dsa_sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32,
                                            _I32, _I32, _F, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -122,8 +122,8 @@ def index_topk_ws_bytes(Sq: int, Sk: int, topk: int, idx_heads: int = 4, q_chunk
     return int(lib().dsa_index_topk_ws_bytes(Sq, Sk, idx_heads, IDX_DIM, POOL, topk, q_chunk))
 
 
-def sparse_attn_bwd_ws_bytes(Sq: int, Sk: int, heads: int) -> int:
-    return int(lib().dsa_sparse_attn_bwd_ws_bytes(Sq, Sk, heads, HEAD_DIM))
+def sparse_attn_bwd_ws_bytes(Sq: int, Sk: int, heads: int, topk: int) -> int:
+    return int(lib().dsa_sparse_attn_bwd_ws_bytes(Sq, Sk, heads, HEAD_DIM, topk))
 
 
 def index_topk(q_idx, k_idx, w_idx, *, topk: int, q_chunk: int = 256, q_pos=None,
@@ -193,7 +193,7 @@ def sparse_attn_bwd(q, k, v, out, dout, lse, idx, *, q_pos=None, scale: float | 
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = int(L.dsa_sparse_attn_bwd_ws_bytes(Sq, Sk, H, D))
+    need = int(L.dsa_sparse_attn_bwd_ws_bytes(Sq, Sk, H, D, idx.shape[1]))
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     st = L.dsa_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(idx),

@@ -6,16 +6,27 @@
 // attention:
 //   P  = exp(scale * q.k - lse)          (recomputed from the saved LSE)
 //   dS = P * (dO.v - Delta),   Delta = sum_d dO * O
-//   dq = scale * dS K    (one query row per wave, written directly)
-//   dk += scale * dS^T q,  dv += P^T dO   (fp32 atomics into the workspace)
+//   dq = scale * dS K,   dk = scale * dS^T q,   dv = P^T dO
 //
-// Mapping: one wave per query row, four rows per workgroup, 32 keys per tile.
-//   S^T  = K . Q^T,  dP^T = V . dO^T          MFMA 16x16x32, keys as M
-//   dQ^T += K^T dS^T                           MFMA 16x16x32, K^T read from LDS
-//   dK[key, dim] = dS[key, head] Q[head, dim]  MFMA 16x16x16, heads as k
-//   dV[key, dim] = P[key, head] dO[head, dim]  MFMA 16x16x16
-// dS and P are transposed through LDS (1 KiB each per tile and wave).
-// Kernels: zero the fp32 accumulators, the row kernel, convert to bf16.
+// Two passes, neither with atomics on the gradients:
+//
+//   dq pass (query-major): one wave per query row, four rows per workgroup,
+//     32 keys per tile, gathered from the row's idx list.  Also saves Delta.
+//       S^T  = K . Q^T,  dP^T = V . dO^T          MFMA 16x16x32, keys as M
+//       dQ^T += K^T dS^T                           MFMA 16x16x32, K^T read from LDS
+//
+//   dk/dv pass (pool-major): the idx lists are inverted first (count per
+//     pool, scan, scatter of the query rows), then one workgroup per pool of
+//     4 keys walks the rows that selected it, 16 (row, head) pairs per step:
+//       S  = Q . K^T,  dP = dO . V^T                MFMA 16x16x32, (row, head) as M,
+//                                                   the pool's keys as N (4 of 16)
+//       dK[key, dim] += dS^T Q,  dV += P^T dO       MFMA 16x16x16, (row, head) as k
+//     The S output layout of the first product is the A-operand layout of the
+//     second, so P and dS go from registers straight into it; Q and dO are
+//     read transposed from LDS (ds_read_b64_tr_b16).  Every key is written
+//     once, in bf16 (0 for keys no row attends).
+//   The order in which a pool's rows are summed follows the scatter (device
+//   atomics), so it is not fixed.
 
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
@@ -26,6 +37,9 @@ namespace {
 constexpr int kD = 128;
 constexpr int kRows = 4;
 constexpr int kKStride = 136;
+
+// ---------------------------------------------------------------------------
+// dq pass
 
 struct BwdArgs {
   const uint16_t* q;
@@ -40,8 +54,7 @@ struct BwdArgs {
   int H, topk;
   float scale, scale_log2;
   uint16_t* dq;
-  float* dk_ws;
-  float* dv_ws;
+  float* stats;            // per (row, head): lse * log2(e), Delta, position (bits), 0
 };
 
 __device__ __forceinline__ int2 slot_info(const int32_t* irow, int ps, int np, int nc, int part,
@@ -60,32 +73,17 @@ __device__ __forceinline__ int2 slot_info(const int32_t* irow, int ps, int np, i
   return make_int2(base, nv);
 }
 
-__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t n4) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n4) reinterpret_cast<f32x4_t*>(p)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ int clamp_pos(const int32_t* q_pos, int64_t r, int64_t Sk) {
+  int64_t pos = r;
+  if (q_pos) {
+    pos = q_pos[r];
+    pos = pos < 0 ? 0 : (pos >= Sk ? Sk - 1 : pos);
+  }
+  return (int)pos;
 }
 
-__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ a,
-                                                      const float* __restrict__ b,
-                                                      uint16_t* __restrict__ oa,
-                                                      uint16_t* __restrict__ ob, int64_t n4) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const f32x4_t x = reinterpret_cast<const f32x4_t*>(a)[i];
-  const f32x4_t y = reinterpret_cast<const f32x4_t*>(b)[i];
-  u32x2_t px, py;
-  px[0] = pack_bf16x2(x[0], x[1]);
-  px[1] = pack_bf16x2(x[2], x[3]);
-  py[0] = pack_bf16x2(y[0], y[1]);
-  py[1] = pack_bf16x2(y[2], y[3]);
-  reinterpret_cast<u32x2_t*>(oa)[i] = px;
-  reinterpret_cast<u32x2_t*>(ob)[i] = py;
-}
-
-__global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __align__(16) uint16_t lds_k[kRows][32 * kKStride];
-  __shared__ __align__(16) uint16_t lds_ds[kRows][32 * 16];
-  __shared__ __align__(16) uint16_t lds_p[kRows][32 * 16];
   __shared__ int2 lds_info[kRows][8];
 
   const int lane = lane_id();
@@ -94,14 +92,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   if (r >= a.Sq) return;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const float NEG_INF = -__builtin_huge_valf();
 
-  int64_t pos64 = r;
-  if (a.q_pos) {
-    pos64 = a.q_pos[r];
-    pos64 = pos64 < 0 ? 0 : (pos64 >= a.Sk ? a.Sk - 1 : pos64);
-  }
-  const int pos = (int)pos64;
+  const int pos = clamp_pos(a.q_pos, r, a.Sk);
   const int nc = (pos + 1) >> 2;
   const int part = (pos + 1) & 3;
   const int32_t* irow = a.idx + r * a.topk;
@@ -141,34 +133,15 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   delta += __shfl_xor(delta, 16, kWave);
   delta += __shfl_xor(delta, 32, kWave);
   const float lse2 = hv ? a.lse[r * a.H + c16] * kLog2e : 0.f;
-
-  // B operands of the 16x16x16 products: [k = head 4g+j][n = dim 16db+c16]
-  s16x4_t QH[8], DH[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    u32x2_t qv, dv;
-    uint32_t qe[4], de[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = 4 * g + j;
-      const int64_t off = (r * a.H + h) * kD + 16 * db + c16;
-      qe[j] = h < a.H ? a.q[off] : 0u;
-      de[j] = h < a.H ? a.dout[off] : 0u;
-    }
-    qv[0] = qe[0] | (qe[1] << 16);
-    qv[1] = qe[2] | (qe[3] << 16);
-    dv[0] = de[0] | (de[1] << 16);
-    dv[1] = de[2] | (de[3] << 16);
-    QH[db] = as_s16x4(qv);
-    DH[db] = as_s16x4(dv);
+  if (hv && g == 0) {
+    f32x4_t rec = {lse2, delta, __int_as_float(pos), 0.f};
+    reinterpret_cast<f32x4_t*>(a.stats)[r * a.H + c16] = rec;
   }
 
   f32x4_t dqa[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) dqa[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint16_t* kt = lds_k[wave];
-  uint16_t* dst_ds = lds_ds[wave];
-  uint16_t* dst_p = lds_p[wave];
   int2* info = lds_info[wave];
 
   for (int t = 0; t < ntile; ++t) {
@@ -194,7 +167,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
       }
     }
 
-    float p[8], ds[8];
+    float ds[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
@@ -207,17 +180,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const float pp = (hv && rr < nv) ? exp2f(s[rr] * a.scale_log2 - lse2) : 0.f;
-        p[4 * kb + rr] = pp;
         ds[4 * kb + rr] = pp * (dp[rr] - delta);
       }
-    }
-
-    // dS^T and P^T (head c16, keys pi(g, j)) -> LDS as [key][head]
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-      dst_ds[key * 16 + c16] = (uint16_t)f32_to_bf16_bits(ds[j]);
-      dst_p[key * 16 + c16] = (uint16_t)f32_to_bf16_bits(p[j]);
     }
     u32x4_t dsb;
     dsb[0] = pack_bf16x2(ds[0], ds[1]);
@@ -240,28 +204,6 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
       ka[3] = (uint32_t)k1[2 * kKStride + 16 * db] | ((uint32_t)k1[3 * kKStride + 16 * db] << 16);
       dqa[db] = mfma32(as_bf16x8(ka), DSB, dqa[db]);
     }
-
-    // dK, dV rows of this tile: D[key 4g+rr][dim 16db+c16] per key block kb
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const s16x4_t Ads = *reinterpret_cast<const s16x4_t*>(dst_ds + (16 * kb + c16) * 16 + 4 * g);
-      const s16x4_t Ap = *reinterpret_cast<const s16x4_t*>(dst_p + (16 * kb + c16) * 16 + 4 * g);
-      const int2 in = info[4 * kb + g];
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4_t dk = mfma16(Ads, QH[db], z);
-        const f32x4_t dv = mfma16(Ap, DH[db], z);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if (rr < in.y) {
-            const int64_t off = (int64_t)(in.x + rr) * kD + 16 * db + c16;
-            unsafeAtomicAdd(a.dk_ws + off, a.scale * dk[rr]);
-            unsafeAtomicAdd(a.dv_ws + off, dv[rr]);
-          }
-        }
-      }
-    }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
@@ -278,17 +220,345 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// inverse of the idx lists: for every pool, the query rows that attend it
+// (selected pools, plus the row's own incomplete pool)
+
+struct InvArgs {
+  const int32_t* idx;
+  const int32_t* q_pos;
+  int64_t Sq, Sk;
+  int topk;
+  int chunks;              // workgroups per row: ceil((topk + 1) / 256)
+  int32_t* offs;           // per pool: count, then (after the scan) start, then end
+  int32_t* list;
+};
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Pool of entry j of row r (j == topk: the row's own incomplete pool), or -1.
+__device__ __forceinline__ int entry_pool(const InvArgs& a, int64_t r, int j) {
+  const int pos = clamp_pos(a.q_pos, r, a.Sk);
+  const int nc = (pos + 1) >> 2;
+  if (j < a.topk) {
+    const int p = a.idx[r * a.topk + j];
+    return (p >= 0 && p < nc) ? p : -1;
+  }
+  return ((pos + 1) & 3) ? nc : -1;
+}
+
+template <bool kScatter>
+__global__ __launch_bounds__(256) void pool_rows_kernel(InvArgs a) {
+  const int64_t r = blockIdx.x / a.chunks;
+  const int j = (int)(blockIdx.x % a.chunks) * 256 + (int)threadIdx.x;
+  if (r >= a.Sq || j > a.topk) return;
+  const int p = entry_pool(a, r, j);
+  if (p < 0) return;
+  if (kScatter) {
+    const int at = atomicAdd(&a.offs[p], 1);
+    a.list[at] = (int32_t)r;
+  } else {
+    atomicAdd(&a.offs[p], 1);
+  }
+}
+
+// Exclusive scan of n counts in place, in blocks of kScanBlock: block sums,
+// a scan of the block sums (one workgroup), then each block's local scan.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_w, int& total) {
+  // 1024 threads: wave scans, then a scan of the 16 wave totals
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(x, o, kWave);
+    if (lane >= o) x += t;
+  }
+  if (lane == kWave - 1) lds_w[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int y = lane < 16 ? lds_w[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int t = __shfl_up(y, o, kWave);
+      if (lane >= o) y += t;
+    }
+    if (lane < 16) lds_w[16 + lane] = y;
+  }
+  __syncthreads();
+  total = lds_w[31];
+  const int before = w > 0 ? lds_w[16 + w - 1] : 0;
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(1024) void scan_block_sums_kernel(const int32_t* __restrict__ c,
+                                                               int32_t* __restrict__ bsum, int64_t n) {
+  __shared__ int lds_w[32];
+  const int64_t base = (int64_t)blockIdx.x * kScanBlock;
+  int v = 0;
+#pragma unroll
+  for (int i = 0; i < kScanBlock / 1024; ++i) {
+    const int64_t j = base + i * 1024 + threadIdx.x;
+    v += j < n ? c[j] : 0;
+  }
+  int total;
+  (void)block_exclusive_scan(v, lds_w, total);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(1024) void scan_sums_kernel(int32_t* __restrict__ bsum, int64_t nb) {
+  __shared__ int lds_w[32];
+  int carry = 0;
+  for (int64_t b0 = 0; b0 < nb; b0 += 1024) {
+    const int64_t j = b0 + threadIdx.x;
+    const int v = j < nb ? bsum[j] : 0;
+    int total;
+    const int ex = block_exclusive_scan(v, lds_w, total);
+    if (j < nb) bsum[j] = carry + ex;
+    carry += total;
+  }
+}
+
+__global__ __launch_bounds__(1024) void scan_apply_kernel(int32_t* __restrict__ c,
+                                                          const int32_t* __restrict__ bsum, int64_t n) {
+  __shared__ int lds_w[32];
+  const int64_t base = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * (kScanBlock / 1024);
+  int v[kScanBlock / 1024];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanBlock / 1024; ++i) {
+    v[i] = base + i < n ? c[base + i] : 0;
+    s += v[i];
+  }
+  int total;
+  int ex = block_exclusive_scan(s, lds_w, total) + bsum[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < kScanBlock / 1024; ++i) {
+    if (base + i < n) c[base + i] = ex;
+    ex += v[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk/dv pass
+
+struct KvArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const f32x4_t* stats;    // per (row, head): lse * log2(e), Delta, position (bits), 0
+  const int32_t* offs;     // per pool: end of its rows in `list` (start = end of the previous)
+  const int32_t* list;
+  int64_t Sk;
+  int H;
+  float scale, scale_log2;
+  uint16_t* dk;
+  uint16_t* dv;
+};
+
+constexpr int kKvWaves = 4;
+constexpr int kTStride = 136;   // LDS row stride (bf16) of the Q / dO tiles
+
+typedef short s16x4a_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4_t read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4a_t*)p);
+}
+
+// Operands of one step (16 (row, head) pairs): the A lanes' Q and dO
+// chunks, and the record of each D-layout pair.
+struct KvStep {
+  u32x4_t q[4], d[4];
+  f32x4_t st[4];
+};
+
+__global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvArgs a) {
+  __shared__ __align__(16) uint16_t lds_q[kKvWaves][16 * kTStride];
+  __shared__ __align__(16) uint16_t lds_do[kKvWaves][16 * kTStride];
+  __shared__ __align__(16) float lds_red[kKvWaves][2][4][kD];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = uniform(tid >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const int64_t p = blockIdx.x;
+  const int beg = p > 0 ? a.offs[p - 1] : 0;
+  const int n = a.offs[p] - beg;
+  const int64_t key0 = 4 * p;
+  const int nkeys = a.Sk - key0 < 4 ? (int)(a.Sk - key0) : 4;
+  const int H = a.H;
+  const int qpc = 16 / H;       // rows per step
+  const int nrh = qpc * H;      // (row, head) pairs per step
+
+  // K, V of the pool as B operands: B[dim 8g + j (+32 ks)][key c16], keys >= nkeys zero
+  bf16x8_t KB[4], VB[4];
+  {
+    const bool kv = c16 < nkeys;
+    const int64_t off = (key0 + c16) * kD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      KB[ks] = kv ? load_bf16x8(a.k + off + 32 * ks) : zero_bf16x8();
+      VB[ks] = kv ? load_bf16x8(a.v + off + 32 * ks) : zero_bf16x8();
+    }
+  }
+  f32x4_t adk[8], adv[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    adk[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    adv[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  uint16_t* tq = lds_q[wave];
+  uint16_t* tdo = lds_do[wave];
+  const int64_t kpos = key0 + c16;   // key of this lane's D column
+  const int toff = (4 * g + (c16 >> 2)) * kTStride + 4 * (c16 & 3);
+
+  // This wave's rows: a contiguous block of the pool's list, read 64 entries
+  // at a time (one per lane) and handed out by shuffles, 16/H rows per step.
+  const int per = (n + kKvWaves - 1) / kKvWaves;
+  const int r0 = min(n, wave * per), r1 = min(n, r0 + per);
+
+  // rows lst (lane j: entry j of the chunk), step s of the chunk, chunk length m
+  auto load_step = [&](int lst, int s, int m, KvStep& o) {
+    const int ja = s * qpc + c16 / H;                   // A lanes: pair c16
+    const bool va = c16 < nrh && ja < m;
+    const int64_t ra = __shfl(lst, ja & 63, kWave);
+    const int64_t aoff = ((va ? ra : 0) * H + c16 % H) * kD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      o.q[ks] = va ? *reinterpret_cast<const u32x4_t*>(a.q + aoff + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+      o.d[ks] = va ? *reinterpret_cast<const u32x4_t*>(a.dout + aoff + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                        // D lanes: pairs 4g + i
+      const int rh = 4 * g + i;
+      const int jd = s * qpc + rh / H;
+      const bool vr = rh < nrh && jd < m;
+      const int64_t rd = __shfl(lst, jd & 63, kWave);
+      o.st[i] = vr ? a.stats[(vr ? rd : 0) * H + rh % H] : f32x4_t{0.f, 0.f, __int_as_float(-1), 0.f};
+    }
+  };
+
+  for (int base = r0; base < r1; base += kWave) {
+    const int m = min(kWave, r1 - base);
+    const int lst = lane < m ? a.list[beg + base + lane] : 0;
+    const int nsteps = (m + qpc - 1) / qpc;
+    KvStep cur, nxt;
+    load_step(lst, 0, m, cur);
+    for (int s = 0; s < nsteps; ++s) {
+      if (s + 1 < nsteps) load_step(lst, s + 1, m, nxt);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        *reinterpret_cast<u32x4_t*>(tq + c16 * kTStride + 8 * g + 32 * ks) = cur.q[ks];
+        *reinterpret_cast<u32x4_t*>(tdo + c16 * kTStride + 8 * g + 32 * ks) = cur.d[ks];
+      }
+      f32x4_t sv = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        sv = mfma32(as_bf16x8(cur.q[ks]), KB[ks], sv);
+        dp = mfma32(as_bf16x8(cur.d[ks]), VB[ks], dp);
+      }
+      // lane holds S[(row, head) 4g+i][key c16]
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = c16 < nkeys && kpos <= (int64_t)__float_as_int(cur.st[i][2]);
+        pv[i] = ok ? exp2f(sv[i] * a.scale_log2 - cur.st[i][0]) : 0.f;
+        dsv[i] = pv[i] * (dp[i] - cur.st[i][1]);
+      }
+      // A operands of the 16x16x16 products: A[key c16][(row, head) 4g+j]
+      u32x2_t pa, dsa;
+      pa[0] = pack_bf16x2(pv[0], pv[1]);
+      pa[1] = pack_bf16x2(pv[2], pv[3]);
+      dsa[0] = pack_bf16x2(dsv[0], dsv[1]);
+      dsa[1] = pack_bf16x2(dsv[2], dsv[3]);
+      const s16x4_t PA = as_s16x4(pa), DSA = as_s16x4(dsa);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // B operands B[(row, head) 4g+j][dim 16db+c16] by transposed reads: lane s
+      // of the group supplies (row 4g + s/4, dims 16db + 4(s%4) .. +3)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const s16x4_t QT = read_tr(tq + toff + 16 * db);
+        const s16x4_t DT = read_tr(tdo + toff + 16 * db);
+        adk[db] = mfma16(DSA, QT, adk[db]);
+        adv[db] = mfma16(PA, DT, adv[db]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      cur = nxt;
+    }
+  }
+
+  // adk[db]: lane holds dK[key 4g+i][dim 16db+c16]; the pool's keys are in g == 0
+  if (g == 0) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lds_red[wave][0][i][16 * db + c16] = adk[db][i];
+        lds_red[wave][1][i][16 * db + c16] = adv[db][i];
+      }
+  }
+  __syncthreads();
+  // 256 threads x 4 consecutive values = 2 x 4 keys x 128 dims
+  {
+    const int which = tid >> 7;            // 0: dk, 1: dv
+    const int key = (tid >> 5) & 3;
+    const int d0 = (tid & 31) * 4;
+    if (key < nkeys) {
+      float v4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kKvWaves; ++w) acc += lds_red[w][which][key][d0 + e];
+        v4[e] = which == 0 ? acc * a.scale : acc;
+      }
+      u32x2_t o;
+      o[0] = pack_bf16x2(v4[0], v4[1]);
+      o[1] = pack_bf16x2(v4[2], v4[3]);
+      uint16_t* dst = (which == 0 ? a.dk : a.dv) + (key0 + key) * kD + d0;
+      *reinterpret_cast<u32x2_t*>(dst) = o;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s) {
+  const BwdWorkspace L = bwd_ws_layout(x.Sq, x.Sk, x.heads, x.topk);
   char* ws = static_cast<char*>(x.ws);
-  float* dk_ws = reinterpret_cast<float*>(ws);
-  float* dv_ws = reinterpret_cast<float*>(ws + align256((size_t)x.Sk * kD * 4));
-  const int64_t n4 = x.Sk * kD / 4;
-  const unsigned eb = (unsigned)((n4 + 255) / 256);
-  zero_f32_kernel<<<dim3(eb), dim3(256), 0, s>>>(dk_ws, n4);
-  zero_f32_kernel<<<dim3(eb), dim3(256), 0, s>>>(dv_ws, n4);
+  float* stats = reinterpret_cast<float*>(ws + L.delta_off);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + L.count_off);
+  int32_t* bsum = reinterpret_cast<int32_t*>(ws + L.bsum_off);
+  int32_t* list = reinterpret_cast<int32_t*>(ws + L.list_off);
+  const int64_t np = bwd_pools(x.Sk);
+  const int64_t nb = (np + kScanBlock - 1) / kScanBlock;
 
+  // inverse of the idx lists
+  fill_i32_kernel<<<dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s>>>(offs, np, 0);
+  InvArgs ia;
+  ia.idx = x.idx;
+  ia.q_pos = x.q_pos;
+  ia.Sq = x.Sq;
+  ia.Sk = x.Sk;
+  ia.topk = x.topk;
+  ia.chunks = (x.topk + 1 + 255) / 256;
+  ia.offs = offs;
+  ia.list = list;
+  const unsigned rb = (unsigned)(x.Sq * ia.chunks);
+  pool_rows_kernel<false><<<dim3(rb), dim3(256), 0, s>>>(ia);
+  scan_block_sums_kernel<<<dim3((unsigned)nb), dim3(1024), 0, s>>>(offs, bsum, np);
+  scan_sums_kernel<<<dim3(1), dim3(1024), 0, s>>>(bsum, nb);
+  scan_apply_kernel<<<dim3((unsigned)nb), dim3(1024), 0, s>>>(offs, bsum, np);
+  pool_rows_kernel<true><<<dim3(rb), dim3(256), 0, s>>>(ia);
+
+  // dq (and Delta)
   BwdArgs a;
   a.q = x.q;
   a.k = x.k;
@@ -305,11 +575,26 @@ hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s) {
   a.scale = x.scale;
   a.scale_log2 = x.scale * kLog2e;
   a.dq = x.out;
-  a.dk_ws = dk_ws;
-  a.dv_ws = dv_ws;
+  a.stats = stats;
   const int64_t blocks = (x.Sq + kRows - 1) / kRows;
-  attn_bwd_kernel<<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
-  to_bf16_kernel<<<dim3(eb), dim3(256), 0, s>>>(dk_ws, dv_ws, x.dk, x.dv, n4);
+  attn_bwd_dq_kernel<<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+
+  // dk, dv
+  KvArgs kv;
+  kv.q = x.q;
+  kv.k = x.k;
+  kv.v = x.v;
+  kv.dout = x.dout;
+  kv.stats = reinterpret_cast<const f32x4_t*>(stats);
+  kv.offs = offs;
+  kv.list = list;
+  kv.Sk = x.Sk;
+  kv.H = x.heads;
+  kv.scale = x.scale;
+  kv.scale_log2 = x.scale * kLog2e;
+  kv.dk = x.dk;
+  kv.dv = x.dv;
+  attn_bwd_dkdv_kernel<<<dim3((unsigned)np), dim3(kKvWaves * kWave), 0, s>>>(kv);
   return hipGetLastError();
 }
 

@@ -167,10 +167,11 @@ DSA_EXPORT int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, 
 }
 
 DSA_EXPORT size_t dsa_sparse_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t heads,
-                                               int32_t head_dim) {
-  (void)Sq; (void)heads;
-  if (Sk < 1 || head_dim != 128) return 0;
-  return dsa::bwd_ws_bytes(Sk);
+                                               int32_t head_dim, int32_t topk) {
+  if (Sq < 1 || Sk < 1 || head_dim != 128 || heads < 1 || heads > 16 || topk < 1 ||
+      topk > dsa::kMaxTopk)
+    return 0;
+  return dsa::bwd_ws_layout(Sq, Sk, heads, topk).total;
 }
 
 DSA_EXPORT int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -193,7 +194,11 @@ DSA_EXPORT int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, 
   if ((st = check_ptr(dv, "dv", 16))) return st;
   if ((st = check_ptr(ws, "ws", 256))) return st;
   if ((st = check_attn_shape(Sq, Sk, heads, head_dim, pool, topk, scale, q_pos))) return st;
-  const size_t need = dsa::bwd_ws_bytes(Sk);
+  // the inverted selection lists are indexed with 32-bit offsets
+  if (Sq * (int64_t)(topk + 1) >= kMaxSeq)
+    return fail(DSA_UNSUPPORTED_SHAPE, "Sq*(topk+1)=%lld must be < 2^31",
+                (long long)(Sq * (int64_t)(topk + 1)));
+  const size_t need = dsa::bwd_ws_layout(Sq, Sk, heads, topk).total;
   if (ws_bytes < need) return fail(DSA_WORKSPACE_TOO_SMALL, "ws_bytes=%zu < %zu", ws_bytes, need);
 
   (void)hipGetLastError();

@@ -31,16 +31,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
-
-// The same rounding (nearest even) by the hardware pack conversion
-// (v_cvt_pk_bf16_f32): one instruction for two values, no branch.
+// Two values at once by the hardware pack conversion (v_cvt_pk_bf16_f32):
+// the same rounding (nearest even), one instruction, no branch.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }

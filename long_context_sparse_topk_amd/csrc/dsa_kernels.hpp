@@ -90,7 +90,29 @@ struct AttnArgs {
   void* ws;               // bwd only
 };
 
-inline size_t bwd_ws_bytes(int64_t Sk) { return align256((size_t)Sk * 128 * 4) * 2; }
+// Backward workspace: per (row, head) a 16-byte record (LSE in log2 units,
+// Delta, position); the per-pool selection counts,
+// turned into list offsets by a scan; the scan's block sums; and the query
+// rows that selected each pool (an inverse of the idx lists).
+constexpr int kScanBlock = 4096;
+
+inline int64_t bwd_pools(int64_t Sk) { return (Sk + 3) / 4; }
+
+struct BwdWorkspace {
+  size_t delta_off, count_off, bsum_off, list_off, total;
+};
+
+inline BwdWorkspace bwd_ws_layout(int64_t Sq, int64_t Sk, int heads, int topk) {
+  BwdWorkspace w;
+  const int64_t np = bwd_pools(Sk);
+  const int64_t nb = (np + kScanBlock - 1) / kScanBlock;
+  w.delta_off = 0;
+  w.count_off = align256((size_t)Sq * heads * 16);
+  w.bsum_off = w.count_off + align256((size_t)np * 4);
+  w.list_off = w.bsum_off + align256((size_t)nb * 4);
+  w.total = w.list_off + align256((size_t)Sq * (topk + 1) * 4);
+  return w;
+}
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s);

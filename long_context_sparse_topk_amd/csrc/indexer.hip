@@ -269,7 +269,7 @@ __device__ __forceinline__ bf16x8_t fold_weight(u32x4_t q, float w) {
   u32x4_t o;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    o[j] = cvt_pk_bf16(bf16_to_f32(q[j] & 0xFFFFu) * w, bf16_to_f32(q[j] >> 16) * w);
+    o[j] = pack_bf16x2(bf16_to_f32(q[j] & 0xFFFFu) * w, bf16_to_f32(q[j] >> 16) * w);
   return as_bf16x8(o);
 }
 

@@ -47,7 +47,10 @@ def test_workspace_sizes():
     assert 0 < a < b < 2 * 2**30          # chunked indexer scratch stays below 2 GiB
     assert D.index_topk_ws_bytes(131072, 131072, 128) < 2**30
     assert D.lib().dsa_index_topk_ws_bytes(10, 10, 4, 64, 4, 0, 1) == 0
-    assert D.sparse_attn_bwd_ws_bytes(10, 1000, 4) >= 2 * 1000 * 128 * 4
+    # Delta (Sq x heads), one offset per pool, the inverted lists (Sq x (topk + 1))
+    assert D.sparse_attn_bwd_ws_bytes(10, 1000, 4, 8) >= 4 * (10 * 4 + 250 + 10 * 9)
+    assert D.sparse_attn_bwd_ws_bytes(131072, 131072, 4, 128) < 2**27
+    assert D.lib().dsa_sparse_attn_bwd_ws_bytes(10, 1000, 4, 128, 0) == 0
 
 
 P = 1 << 20  # a fake, 16-byte aligned address: validation fails before any use
@@ -121,6 +124,9 @@ def test_bwd_validation():
     assert L.dsa_sparse_attn_bwd(*a) == 3 and b"ws_bytes=1000" in L.dsa_last_error()
     a = list(args); a[11] = 256
     assert L.dsa_sparse_attn_bwd(*a) == 2
+    # the inverted selection lists use 32-bit offsets
+    a = list(args); a[8] = 1 << 21; a[9] = 1 << 22; a[13] = 1024
+    assert L.dsa_sparse_attn_bwd(*a) == 2 and b"Sq*(topk+1)" in L.dsa_last_error()
 
 
 def test_python_binding_checks_dtypes():
