@@ -192,16 +192,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
 
-    // dQ^T[dim, head] += K^T[dim, key] dS^T[key, head]
-    const uint16_t* k0 = kt + (4 * g) * kKStride + c16;
-    const uint16_t* k1 = kt + (16 + 4 * g) * kKStride + c16;
+    // dQ^T[dim, head] += K^T[dim, key] dS^T[key, head]; the A operand holds
+    // keys 4g..4g+3 then 16+4g..16+4g+3 (the keys of this lane's dS values)
+    const uint16_t* k0 = kt + 4 * g * kKStride + tr_offset(c16, kKStride);
+    const uint16_t* k1 = k0 + 16 * kKStride;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      u32x4_t ka;
-      ka[0] = (uint32_t)k0[0 * kKStride + 16 * db] | ((uint32_t)k0[1 * kKStride + 16 * db] << 16);
-      ka[1] = (uint32_t)k0[2 * kKStride + 16 * db] | ((uint32_t)k0[3 * kKStride + 16 * db] << 16);
-      ka[2] = (uint32_t)k1[0 * kKStride + 16 * db] | ((uint32_t)k1[1 * kKStride + 16 * db] << 16);
-      ka[3] = (uint32_t)k1[2 * kKStride + 16 * db] | ((uint32_t)k1[3 * kKStride + 16 * db] << 16);
+      const u32x2_t lo = __builtin_bit_cast(u32x2_t, read_tr(k0 + 16 * db));
+      const u32x2_t hi = __builtin_bit_cast(u32x2_t, read_tr(k1 + 16 * db));
+      const u32x4_t ka = {lo[0], lo[1], hi[0], hi[1]};
       dqa[db] = mfma32(as_bf16x8(ka), DSB, dqa[db]);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -363,12 +362,6 @@ struct KvArgs {
 constexpr int kKvWaves = 4;
 constexpr int kTStride = 136;   // LDS row stride (bf16) of the Q / dO tiles
 
-typedef short s16x4a_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ s16x4_t read_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4a_t*)p);
-}
-
 // Operands of one step (16 (row, head) pairs): the A lanes' Q and dO
 // chunks, and the record of each D-layout pair.
 struct KvStep {
@@ -415,7 +408,7 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
   uint16_t* tq = lds_q[wave];
   uint16_t* tdo = lds_do[wave];
   const int64_t kpos = key0 + c16;   // key of this lane's D column
-  const int toff = (4 * g + (c16 >> 2)) * kTStride + 4 * (c16 & 3);
+  const int toff = 4 * g * kTStride + tr_offset(c16, kTStride);
 
   // This wave's rows: a contiguous block of the pool's list, read 64 entries
   // at a time (one per lane) and handed out by shuffles, 16/H rows per step.

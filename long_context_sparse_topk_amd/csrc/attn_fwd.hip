@@ -174,16 +174,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
 
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    // V^T operand: row = dim 16*db + c16, k slot j -> key 4g+j (j<4) or 16+4g+(j-4)
-    const uint16_t* v0 = vt + (4 * g) * kVStride + c16;
-    const uint16_t* v1 = vt + (16 + 4 * g) * kVStride + c16;
+    // V^T operand: row = dim 16*db + c16, k slot j -> key 4g+j (j<4) or
+    // 16+4g+(j-4), read transposed from the [key][dim] tile
+    const uint16_t* v0 = vt + 4 * g * kVStride + tr_offset(c16, kVStride);
+    const uint16_t* v1 = v0 + 16 * kVStride;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      u32x4_t va;
-      va[0] = (uint32_t)v0[0 * kVStride + 16 * db] | ((uint32_t)v0[1 * kVStride + 16 * db] << 16);
-      va[1] = (uint32_t)v0[2 * kVStride + 16 * db] | ((uint32_t)v0[3 * kVStride + 16 * db] << 16);
-      va[2] = (uint32_t)v1[0 * kVStride + 16 * db] | ((uint32_t)v1[1 * kVStride + 16 * db] << 16);
-      va[3] = (uint32_t)v1[2 * kVStride + 16 * db] | ((uint32_t)v1[3 * kVStride + 16 * db] << 16);
+      const u32x2_t lo = __builtin_bit_cast(u32x2_t, read_tr(v0 + 16 * db));
+      const u32x2_t hi = __builtin_bit_cast(u32x2_t, read_tr(v1 + 16 * db));
+      const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
       acc[db] = mfma32(as_bf16x8(va), PB, acc[db]);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");

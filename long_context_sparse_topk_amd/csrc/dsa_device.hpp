@@ -89,6 +89,23 @@ __device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
 }
 
 // ---------------------------------------------------------------------------
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i%4 of the 8-byte chunks addressed by lanes
+// i/4 + 4j, j = 0..3.  So if lane s of the group addresses row R0 + s/4 and
+// columns C0 + 4(s%4) .. +3 of a row-major bf16 tile, lane i receives column
+// C0 + i of rows R0 .. R0+3: a 4-value MFMA operand read across rows.
+
+typedef short s16x4_lds_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4_t read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_lds_t*)p);
+}
+
+// Offset (in elements) of the chunk lane c16 addresses for read_tr from a
+// tile with row stride `stride`: row c16/4, columns 4*(c16%4).
+__device__ __forceinline__ int tr_offset(int c16, int stride) { return (c16 >> 2) * stride + 4 * (c16 & 3); }
+
+// ---------------------------------------------------------------------------
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // orders global memory, which on this ISA (loads and stores share one
 // counter) waits for every global load in flight, prefetches included.

@@ -228,6 +228,21 @@ def test_dense_equivalence_against_torch():
     assert_close("dense O", got["out"], ref.permute(1, 0, 2).double().cpu().numpy())
 
 
+@pytest.mark.parametrize("S,H", [(1030, 5), (700, 16)])
+def test_backward_dense_selection_long_pool_lists(S, H):
+    # every query selects every complete pool, so pool 0 is attended by about
+    # S rows: the pool-major dk/dv pass walks lists far longer than one
+    # 64-row chunk per wave; H = 5 leaves one (row, head) pair of each step
+    # unused, H = 16 gives one row per step
+    d = _attn_inputs(S, S, H, seed=S + 31 * H)
+    topk = S // 4
+    idx = np.full((S, topk), -1, np.int32)
+    for i in range(S):
+        idx[i, :(i + 1) // 4] = np.arange((i + 1) // 4)
+    got = gpu_attn(d, idx)
+    _check_attn(f"dense S={S} H={H}", got, d, idx, None)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads (launch configuration of the benchmark), sampled checks
 
