@@ -12,6 +12,9 @@ constexpr int kIndexQueryTile = 64;     // queries per workgroup sub-tile
 constexpr int kIndexPoolTile = 64;      // pools per LDS-staged key tile
 constexpr int kIndexMaxSlots = 512;     // workgroups owning candidate lists (2 per CU x 256 CUs)
 constexpr int kMaxTopk = 2048;
+// device counters at the head of the fallback region: [0] fallback-list
+// length, [1] and [2] the tile queues of the two-phase and the exact pass
+constexpr int kIndexCounters = 3;
 
 // Survivors of the running threshold are staged in LDS per (wave, row block
 // of 4 queries) and moved to the per-query lists in HBM when a stage is
@@ -52,7 +55,7 @@ inline IndexWorkspace index_ws_layout(int64_t Sq, int64_t Sk, int topk) {
   const size_t cand = (size_t)index_slots(Sq) * kIndexQueryTile * index_candidate_cap(topk);
   w.kpool_off = 0;
   w.cand_off = align256((size_t)index_padded_pools(Sk) * 64 * 2);
-  w.fb_off = w.cand_off + align256(cand * 8);          // fallback count + rows
+  w.fb_off = w.cand_off + align256(cand * 8);          // counters (256 B), fallback rows
   w.total = w.fb_off + 256 + align256((size_t)Sq * 4);
   return w;
 }

@@ -52,13 +52,17 @@ constexpr int kRing = 3;                   // LDS key-tile buffers
 
 // Pools [n_pools, n_padded) are zero-filled so that key tiles can be loaded
 // whole, without bounds predicates.
-// Thread 0 also clears the indexer's fallback-list length.
+// Thread 0 also clears the indexer's counters: the fallback-list length and
+// the tile queues of the two passes.
 __global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restrict__ k_idx,
                                                         uint16_t* __restrict__ kpool,
                                                         int64_t n_pools, int64_t n_padded,
                                                         uint32_t* __restrict__ fb_count) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t == 0) *fb_count = 0u;
+  if (t == 0) {
+#pragma unroll
+    for (int j = 0; j < kIndexCounters; ++j) fb_count[j] = 0u;
+  }
   if (t >= n_padded * 8) return;
   const int64_t p = t >> 3;
   const int c = (int)(t & 7);
@@ -220,12 +224,6 @@ __device__ __forceinline__ float select_and_compact(u32x2_t* __restrict__ list, 
   return key_to_float(T);
 }
 
-// Tile order: each workgroup takes every gridDim-th tile, snaking, over tiles
-// ranked from the longest causal range down (the last query tiles when q_pos
-// is the identity).
-__device__ __forceinline__ int64_t snake_rank(int64_t it, int slot, int nslots) {
-  return (it & 1) ? it * nslots + (nslots - 1 - slot) : it * nslots + slot;
-}
 
 struct KernelArgs {
   const uint16_t* q_idx;
@@ -239,6 +237,7 @@ struct KernelArgs {
   const uint32_t* nrows;   // exact pass: device count of rows
   uint32_t* fb_count;      // two-phase pass: fallback list length
   int32_t* fb_rows;        // two-phase pass: fallback list
+  uint32_t* tile_next;     // this pass's tile queue (next tile rank)
   u32x2_t* cand;           // [slots][kQT][cap] (order key, pool id)
   int32_t* idx_out;
 };
@@ -246,10 +245,14 @@ struct KernelArgs {
 // Phase-1 sample: every kSampleStride-th pool tile.  With a fraction f of a
 // query's causal pools sampled, about r/f pools score at or above the r-th
 // best sampled score, with a spread of about sqrt(r)/f; r is the smallest
-// value with r - kSampleZ sqrt(r) >= k f, kSampleZ spreads of margin before
-// the query needs the exact pass.
+// value with r - z sqrt(r) >= k f, z spreads of margin.  A small margin
+// keeps fewer survivors (a cheaper phase 2) and fails more often: phase 2
+// runs with kSampleZ1 and, in a workgroup where some query failed, once more
+// for those queries with kSampleZ2; a query failing twice goes to the exact
+// pass.
 constexpr int kSampleStride = 16;
-constexpr float kSampleZ = 5.f;
+constexpr float kSampleZ1 = 3.f;
+constexpr float kSampleZ2 = 5.f;
 constexpr int kSampleKeep = 8;   // sampled scores kept per lane and query
 
 constexpr int kStage = kIndexStage;
@@ -278,8 +281,9 @@ __device__ __forceinline__ bf16x8_t fold_weight(u32x4_t q, float w) {
 // streams every tile keeping pools with score >= t, then the running top-k.
 // If at least min(k, n_c) pools score >= t, every true top-k pool does (its
 // score is >= the k-th best score >= t), so the result is exact; otherwise
-// the query goes to the fallback list, which the exact pass (!kTwoPhase:
-// one phase, threshold from -inf) then scores.
+// phase 2 is run again with a lower threshold from the same sample, and a
+// query that fails that too goes to the fallback list, which the exact pass
+// (!kTwoPhase: one phase, threshold from -inf) then scores.
 //
 // Scores: the head weight is folded into the query operand, bf16(w_h q_h),
 // so w_h ReLU(q_h . k) = clamp_h(bf16(w_h q_h) . k) with clamp_h = max(., 0)
@@ -298,6 +302,8 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
   __shared__ __align__(16) u32x4_t lds_k[kRing][kPT * 8];   // ring of (64 pools x 128 B), swizzled
   __shared__ uint32_t lds_st[kWaves][4][2][kStage];  // stage: [0] score bits, [1] (query tag, pool id)
   __shared__ int lds_np[kWaves];
+  __shared__ uint32_t lds_fail[kWaves];
+  __shared__ int lds_tile;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -318,8 +324,15 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     dma_off[j] = (pr * 8 + ((p & 7) ^ (pr & 7))) * 16;
   }
 
-  for (int64_t it = 0;; ++it) {
-    const int64_t rank = snake_rank(it, blockIdx.x, gridDim.x);
+  // Tiles come from a queue shared by the grid, ranked from the longest
+  // causal range down (the last query tiles when q_pos is the identity): the
+  // greedy order balances the uneven tile costs, retries included.  Thread 0
+  // takes the next rank while the current tile is scored; the barrier at the
+  // end of the tile publishes it.
+  if (tid == 0) lds_tile = (int)atomicAdd(a.tile_next, 1u);
+  lds_barrier();
+  for (;;) {
+    const int64_t rank = lds_tile;
     if (rank >= ntiles) break;
     const int64_t q0 = (kTwoPhase ? ntiles - 1 - rank : rank) * kQT;
     auto row_of = [&](int64_t i) -> int64_t {
@@ -371,10 +384,12 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     ncmin = uniform(ncmin);
     if (lane == 0) lds_np[wave] = ncm;
     lds_barrier();
+    if (tid == 0) lds_tile = (int)atomicAdd(a.tile_next, 1u);  // read after the tile
     const int tp = max(max(lds_np[0], lds_np[1]), max(lds_np[2], lds_np[3]));
     const int ntp = (tp + kPT - 1) / kPT;   // pool tiles in the tile's causal range
 
     float tau[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    float tau2[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};  // the retry's thresholds
     const int64_t wbase = ((int64_t)blockIdx.x * kQT + 16 * wave) * cap;
 
     // Pool-key tiles go straight from HBM to LDS (buffer loads with the LDS
@@ -465,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       // Phase 1: each lane keeps, per query, the 8 best sampled scores of
       // its pool column (descending, in registers).  Their union holds at
       // most every sampled score, so its r-th best is at most the sample's.
-      int rq[4];
+      int rq[2][4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         // r from the fraction f of the query's causal pools the sample
@@ -473,14 +488,18 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         const int n_full = nc[rb] / kPT, part = nc[rb] % kPT;
         const int s_q = kPT * ((n_full + kSampleStride - 1) / kSampleStride) +
                         (n_full % kSampleStride == 0 ? part : 0);
-        int r = 0;
-        if (nc[rb] > topk && s_q > 0) {
-          const float f = (float)s_q / (float)nc[rb];
-          const float x = 0.5f * (kSampleZ + sqrtf(kSampleZ * kSampleZ + 4.f * topk * f));
-          r = (int)ceilf(x * x);
-          if (r >= s_q || r > kSampleKeep * 16 * 3 / 4) r = 0;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float z = m == 0 ? kSampleZ1 : kSampleZ2;
+          int r = 0;
+          if (nc[rb] > topk && s_q > 0) {
+            const float f = (float)s_q / (float)nc[rb];
+            const float x = 0.5f * (z + sqrtf(z * z + 4.f * topk * f));
+            r = (int)ceilf(x * x);
+            if (r >= s_q || r > kSampleKeep * 16 * 3 / 4) r = 0;
+          }
+          rq[m][rb] = r;
         }
-        rq[rb] = r;
       }
       float best[4][kSampleKeep];
 #pragma unroll
@@ -511,187 +530,214 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         uint32_t kk[kSampleKeep];
 #pragma unroll
         for (int j = 0; j < kSampleKeep; ++j) kk[j] = order_key(best[rb][j] + 0.f);
-        uint32_t pre_k = 0u;
-        for (int b = 31; b >= 0; --b) {
-          const uint32_t cand_k = pre_k | (1u << b);
-          int c = 0;
 #pragma unroll
-          for (int j = 0; j < kSampleKeep; ++j) c += kk[j] >= cand_k ? 1 : 0;
-          c += __shfl_xor(c, 1, kWave);
-          c += __shfl_xor(c, 2, kWave);
-          c += __shfl_xor(c, 4, kWave);
-          c += __shfl_xor(c, 8, kWave);
-          if (c >= rq[rb]) pre_k = cand_k;
+        for (int m = 0; m < 2; ++m) {
+          const int r = rq[m][rb];
+          uint32_t pre_k = 0u;
+          for (int b = 31; b >= 0; --b) {
+            const uint32_t cand_k = pre_k | (1u << b);
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < kSampleKeep; ++j) c += kk[j] >= cand_k ? 1 : 0;
+            c += __shfl_xor(c, 1, kWave);
+            c += __shfl_xor(c, 2, kWave);
+            c += __shfl_xor(c, 4, kWave);
+            c += __shfl_xor(c, 8, kWave);
+            if (c >= r) pre_k = cand_k;
+          }
+          const float t = r > 0 ? float_below(key_to_float(pre_k)) : NEG_INF;
+          if (m == 0) tau[rb] = t;
+          else tau2[rb] = t;
         }
-        tau[rb] = rq[rb] > 0 ? float_below(key_to_float(pre_k)) : NEG_INF;
       }
     }
 
     // Phase 2 (or the exact pass): every tile; survivors of the running
     // threshold are staged, stages are flushed to the per-query lists, and a
     // list that a flush leaves within one stage of its end keeps its top-k.
-    int nst[4] = {0, 0, 0, 0};   // staged entries per row block (wave-uniform)
-    int cnt_v = 0;               // lane q < 16: list length of wave query q = 4*rb + t
-
-    // Entry j of stage rb (of n) is moved to the list of its query; `c` holds
-    // the 4 list lengths of the row block and advances (stable per query).
-    auto place = [&](int rb, int j0, int n, uint32_t fbits, uint32_t id, int (&c)[4]) {
-      const bool valid = j0 + lane < n;
-      const int t = (int)(id >> kTagShift);
-      int pos = 0;
-#pragma unroll
-      for (int tq = 0; tq < 4; ++tq) {
-        const bool mine = valid && t == tq;
-        const uint64_t Mt = ballot(mine);
-        if (mine) pos = c[tq] + mbcnt(Mt);
-        c[tq] += __popcll(Mt);
-      }
-      if (valid) {
-        u32x2_t e;
-        e[0] = order_key(__uint_as_float(fbits) + 0.f);  // -0 -> +0
-        e[1] = id & kPoolMask;
-        a.cand[wbase + (int64_t)(4 * rb + t) * cap + pos] = e;
-      }
-    };
-    // Move the stages flagged in fl to the lists.  The first 64 entries of
-    // every flagged stage are read before any is placed, so one LDS latency
-    // covers them all.
-    auto flush = [&](uint32_t fl) {
-      uint32_t f0[4], i0[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        f0[rb] = 0u;
-        i0[rb] = 0u;
-        if ((fl >> rb) & 1u) {
-          if (lane < nst[rb]) {
-            f0[rb] = lds_st[wave][rb][0][lane];
-            i0[rb] = lds_st[wave][rb][1][lane];
-          }
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (!((fl >> rb) & 1u)) continue;
-        const int n = nst[rb];
-        int c[4];
-#pragma unroll
-        for (int tq = 0; tq < 4; ++tq) c[tq] = __builtin_amdgcn_readlane(cnt_v, 4 * rb + tq);
-        place(rb, 0, n, f0[rb], i0[rb], c);
-        for (int j0 = kWave; j0 < n; j0 += kWave) {
-          const int j = j0 + lane;
-          const uint32_t fb = j < n ? lds_st[wave][rb][0][j] : 0u;
-          const uint32_t id = j < n ? lds_st[wave][rb][1][j] : 0u;
-          place(rb, j0, n, fb, id, c);
-        }
-#pragma unroll
-        for (int tq = 0; tq < 4; ++tq) cnt_v = lane == 4 * rb + tq ? c[tq] : cnt_v;
-        nst[rb] = 0;
-      }
-    };
-
-    stream(0, 1,
-        [&](int i) {
-          // A flush costs about one store latency, whatever its size, and a
-          // wave that flushes holds up the others at the next barrier.  So
-          // all 4 stages of a wave are flushed together, when one of them
-          // could not take another tile's worth (4 x 64 entries), and every
-          // kFlushPeriod tiles (the same tiles in every wave).
-          bool full = false;
-          uint32_t fl = 0;
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            full |= nst[rb] > kStage - 4 * kWave;
-            fl |= nst[rb] > 0 ? 1u << rb : 0u;
-          }
-          if (!(full || (i > 0 && (i % kFlushPeriod) == 0)) || fl == 0) return;
-          flush(fl);
-          bool fenced = false;
-          for (uint32_t m = fl; m != 0; m &= m - 1) {
-            const int rb = __builtin_ctz(m);
+    // A workgroup with a query whose threshold turned out too high runs the
+    // pass once more, for those queries only, with the larger margin
+    // (threshold +inf for the others); `redo` holds the wave's queries
+    // (bit 4*rb + t) scored in the current attempt.
+    uint32_t redo = 0xFFFFu;
 #pragma unroll 1
-            for (int tq = 0; tq < 4; ++tq) {
-              const int q = 4 * rb + tq;
-              const int n = __builtin_amdgcn_readlane(cnt_v, q);
-              if (n <= cap - kStage) continue;
-              if (!fenced) {
-                __threadfence_block();  // this wave's list stores are visible
-                fenced = true;
-              }
-              // the (just flushed, empty) stage of rb holds the histogram
-              const float T = select_and_compact(a.cand + wbase + (int64_t)q * cap, n, topk,
-                                                 lds_st[wave][rb][0], nullptr);
-              cnt_v = lane == q ? topk : cnt_v;
+    for (int attempt = 0;; ++attempt) {
+      if (attempt > 0) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (r == rb && g == tq) tau[r] = T;
+        for (int rb = 0; rb < 4; ++rb)
+          tau[rb] = ((redo >> (4 * rb + g)) & 1u) ? tau2[rb] : POS_INF;
+      }
+      int nst[4] = {0, 0, 0, 0};   // staged entries per row block (wave-uniform)
+      int cnt_v = 0;               // lane q < 16: list length of wave query q = 4*rb + t
+
+      // Entry j of stage rb (of n) is moved to the list of its query; `c` holds
+      // the 4 list lengths of the row block and advances (stable per query).
+      auto place = [&](int rb, int j0, int n, uint32_t fbits, uint32_t id, int (&c)[4]) {
+        const bool valid = j0 + lane < n;
+        const int t = (int)(id >> kTagShift);
+        int pos = 0;
+#pragma unroll
+        for (int tq = 0; tq < 4; ++tq) {
+          const bool mine = valid && t == tq;
+          const uint64_t Mt = ballot(mine);
+          if (mine) pos = c[tq] + mbcnt(Mt);
+          c[tq] += __popcll(Mt);
+        }
+        if (valid) {
+          u32x2_t e;
+          e[0] = order_key(__uint_as_float(fbits) + 0.f);  // -0 -> +0
+          e[1] = id & kPoolMask;
+          a.cand[wbase + (int64_t)(4 * rb + t) * cap + pos] = e;
+        }
+      };
+      // Move the stages flagged in fl to the lists.  The first 64 entries of
+      // every flagged stage are read before any is placed, so one LDS latency
+      // covers them all.
+      auto flush = [&](uint32_t fl) {
+        uint32_t f0[4], i0[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          f0[rb] = 0u;
+          i0[rb] = 0u;
+          if ((fl >> rb) & 1u) {
+            if (lane < nst[rb]) {
+              f0[rb] = lds_st[wave][rb][0][lane];
+              i0[rb] = lds_st[wave][rb][1][lane];
             }
           }
-        },
-        [&](float (&sc)[4][4], int pt0) {
+        }
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < 4; ++rb) {
+          if (!((fl >> rb) & 1u)) continue;
+          const int n = nst[rb];
+          int c[4];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-              const bool keep = sc[rb][cb] > tau[rb];
-              const uint64_t M = ballot(keep);
-              if (M) {
-                if (keep) {
-                  const int slot = nst[rb] + mbcnt(M);
-                  uint32_t* st = &lds_st[wave][rb][0][slot];
-                  st[0] = __float_as_uint(sc[rb][cb]);
-                  st[kStage] = (uint32_t)(pt0 + 16 * cb) + lane_tag;
+          for (int tq = 0; tq < 4; ++tq) c[tq] = __builtin_amdgcn_readlane(cnt_v, 4 * rb + tq);
+          place(rb, 0, n, f0[rb], i0[rb], c);
+          for (int j0 = kWave; j0 < n; j0 += kWave) {
+            const int j = j0 + lane;
+            const uint32_t fb = j < n ? lds_st[wave][rb][0][j] : 0u;
+            const uint32_t id = j < n ? lds_st[wave][rb][1][j] : 0u;
+            place(rb, j0, n, fb, id, c);
+          }
+#pragma unroll
+          for (int tq = 0; tq < 4; ++tq) cnt_v = lane == 4 * rb + tq ? c[tq] : cnt_v;
+          nst[rb] = 0;
+        }
+      };
+
+      stream(0, 1,
+          [&](int i) {
+            // A flush costs about one store latency, whatever its size, and a
+            // wave that flushes holds up the others at the next barrier.  So
+            // all 4 stages of a wave are flushed together, when one of them
+            // could not take another tile's worth (4 x 64 entries), and every
+            // kFlushPeriod tiles (the same tiles in every wave).
+            bool full = false;
+            uint32_t fl = 0;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+              full |= nst[rb] > kStage - 4 * kWave;
+              fl |= nst[rb] > 0 ? 1u << rb : 0u;
+            }
+            if (!(full || (i > 0 && (i % kFlushPeriod) == 0)) || fl == 0) return;
+            flush(fl);
+            bool fenced = false;
+            for (uint32_t m = fl; m != 0; m &= m - 1) {
+              const int rb = __builtin_ctz(m);
+#pragma unroll 1
+              for (int tq = 0; tq < 4; ++tq) {
+                const int q = 4 * rb + tq;
+                const int n = __builtin_amdgcn_readlane(cnt_v, q);
+                if (n <= cap - kStage) continue;
+                if (!fenced) {
+                  __threadfence_block();  // this wave's list stores are visible
+                  fenced = true;
                 }
-                nst[rb] += __popcll(M);
+                // the (just flushed, empty) stage of rb holds the histogram
+                const float T = select_and_compact(a.cand + wbase + (int64_t)q * cap, n, topk,
+                                                   lds_st[wave][rb][0], nullptr);
+                cnt_v = lane == q ? topk : cnt_v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (r == rb && g == tq) tau[r] = T;
               }
             }
-          }
-        });
+          },
+          [&](float (&sc)[4][4], int pt0) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+              for (int cb = 0; cb < 4; ++cb) {
+                const bool keep = sc[rb][cb] > tau[rb];
+                const uint64_t M = ballot(keep);
+                if (M) {
+                  if (keep) {
+                    const int slot = nst[rb] + mbcnt(M);
+                    uint32_t* st = &lds_st[wave][rb][0][slot];
+                    st[0] = __float_as_uint(sc[rb][cb]);
+                    st[kStage] = (uint32_t)(pt0 + 16 * cb) + lane_tag;
+                  }
+                  nst[rb] += __popcll(M);
+                }
+              }
+            }
+          });
 
-    // remaining stages, then the final selection written to the output rows
-    {
-      uint32_t fl = 0;
+      // remaining stages, then the final selection written to the output rows
+      {
+        uint32_t fl = 0;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) fl |= nst[rb] > 0 ? 1u << rb : 0u;
-      if (fl) flush(fl);
-    }
-    __threadfence_block();
-#pragma unroll 1
-    for (int q = 0; q < 16; ++q) {
-      const int64_t qr = row_of(q0 + 16 * wave + q);
-      if (qr < 0) continue;
-      const int rb = q >> 2;
-      const int n = __builtin_amdgcn_readlane(cnt_v, q);
-      const int ncr = rb == 0 ? nc[0] : rb == 1 ? nc[1] : rb == 2 ? nc[2] : nc[3];
-      const int need = min(topk, __shfl(ncr, 16 * (q & 3), kWave));
-      if (kTwoPhase && n < need) {  // threshold estimate too high
-        if (lane == 0) a.fb_rows[atomicAdd(a.fb_count, 1u)] = (int32_t)qr;
-        continue;
+        for (int rb = 0; rb < 4; ++rb) fl |= nst[rb] > 0 ? 1u << rb : 0u;
+        if (fl) flush(fl);
       }
-      const int64_t base = wbase + (int64_t)q * cap;
-      int32_t* dst = a.idx_out + qr * topk;
-      int filled = n;
-      if (n > topk) {
-        select_and_compact(a.cand + base, n, topk, lds_st[wave][0][0], dst);  // stages are empty
-        filled = topk;
-      } else {
-        const u32x2_t* src = a.cand + base;
-        for (int j0 = 0; j0 < n; j0 += 8 * kWave) {
-          int32_t v[8];
+      __threadfence_block();
+      uint32_t failed = 0;  // wave queries whose threshold was too high
+#pragma unroll 1
+      for (int q = 0; q < 16; ++q) {
+        if (!((redo >> q) & 1u)) continue;
+        const int64_t qr = row_of(q0 + 16 * wave + q);
+        if (qr < 0) continue;
+        const int rb = q >> 2;
+        const int n = __builtin_amdgcn_readlane(cnt_v, q);
+        const int ncr = rb == 0 ? nc[0] : rb == 1 ? nc[1] : rb == 2 ? nc[2] : nc[3];
+        const int need = min(topk, __shfl(ncr, 16 * (q & 3), kWave));
+        if (kTwoPhase && n < need) {  // threshold estimate too high
+          if (attempt == 0) failed |= 1u << q;
+          else if (lane == 0) a.fb_rows[atomicAdd(a.fb_count, 1u)] = (int32_t)qr;
+          continue;
+        }
+        const int64_t base = wbase + (int64_t)q * cap;
+        int32_t* dst = a.idx_out + qr * topk;
+        int filled = n;
+        if (n > topk) {
+          select_and_compact(a.cand + base, n, topk, lds_st[wave][0][0], dst);  // stages are empty
+          filled = topk;
+        } else {
+          const u32x2_t* src = a.cand + base;
+          for (int j0 = 0; j0 < n; j0 += 8 * kWave) {
+            int32_t v[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int j = j0 + i * kWave + lane;
-            v[i] = j < n ? (int32_t)src[j][1] : 0;
-          }
+            for (int i = 0; i < 8; ++i) {
+              const int j = j0 + i * kWave + lane;
+              v[i] = j < n ? (int32_t)src[j][1] : 0;
+            }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int j = j0 + i * kWave + lane;
-            if (j < n) dst[j] = v[i];
+            for (int i = 0; i < 8; ++i) {
+              const int j = j0 + i * kWave + lane;
+              if (j < n) dst[j] = v[i];
+            }
           }
         }
+        for (int j = filled + lane; j < topk; j += kWave) dst[j] = -1;
       }
-      for (int j = filled + lane; j < topk; j += kWave) dst[j] = -1;
+      if (!kTwoPhase || attempt > 0) break;
+      if (lane == 0) lds_fail[wave] = failed;
+      lds_barrier();
+      if ((lds_fail[0] | lds_fail[1] | lds_fail[2] | lds_fail[3]) == 0u) break;
+      redo = failed;
     }
-    lds_barrier();  // lds_np reuse in the next tile
+    lds_barrier();  // publishes lds_tile; lds_np is reused in the next tile
   }
 }
 
@@ -723,7 +769,7 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   const IndexWorkspace L = index_ws_layout(ia.Sq, ia.Sk, ia.topk);
   char* ws = static_cast<char*>(ia.ws);
   uint16_t* kpool = reinterpret_cast<uint16_t*>(ws + L.kpool_off);
-  uint32_t* fb_count = reinterpret_cast<uint32_t*>(ws + L.fb_off);
+  uint32_t* fb_count = reinterpret_cast<uint32_t*>(ws + L.fb_off);  // kIndexCounters counters
   int32_t* fb_rows = reinterpret_cast<int32_t*>(ws + L.fb_off + 256);
   const int64_t n_pools = ia.Sk / 4;
   const int64_t n_padded = index_padded_pools(ia.Sk);
@@ -752,8 +798,10 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   int64_t slots = index_slots(ia.Sq);  // the workspace holds candidate lists for this many
   const int64_t resident = resident_index_blocks();
   if (resident < slots) slots = resident;
+  a.tile_next = fb_count + 1;
   indexer_topk_kernel<true><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
-  // queries whose threshold estimate was too high, scored exactly
+  // queries whose threshold estimate was too high twice, scored exactly
+  a.tile_next = fb_count + 2;
   indexer_topk_kernel<false><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }

@@ -135,6 +135,46 @@ def test_index_subset_positions_sk_larger():
     assert_idx_equal("idx subset", got, ref)
 
 
+def _threshold_trap_keys(S, unsampled):
+    """Indexer keys for q = w = 1, where the score of pool p is 4 * T(p).
+
+    The indexer estimates each query's threshold from a sample of every 16th
+    tile of 64 pools (tiles 0, 16, 32, ...).  Here tile 0 holds the best
+    scores, T = 150 - p, the other sampled tiles T = 50, and every pool
+    outside the sample T = `unsampled`, so the sample overstates how good the
+    unsampled pools are.  With `unsampled` = 125 the small-margin threshold of
+    long queries (about the 18th best sampled score) keeps fewer than k pools
+    and the larger-margin retry (about the 34th) keeps every unsampled pool;
+    with 10 both keep fewer than k and those rows need the exact pass.
+    """
+    n = S // 4
+    T = np.full(n, unsampled)
+    tile = np.arange(n) // 64
+    T[tile % 16 == 0] = 50
+    T[:64] = 150 - np.arange(64)
+    kp = np.clip(T[:, None] - 3 * np.arange(64)[None, :], 0, 3)   # row sums = T
+    return _bits(np.repeat(kp, 4, axis=0).astype(np.float32))
+
+
+@pytest.mark.parametrize("unsampled", [125, 10])
+@pytest.mark.parametrize("permute", [False, True])
+def test_index_sampled_threshold_too_high(unsampled, permute):
+    # every query row needs its own fallback: a retry, or the exact pass; with
+    # permuted positions a workgroup mixes rows that fail with rows that do not
+    S, topk = 10240, 64
+    k_idx = _threshold_trap_keys(S, unsampled)
+    q = _bits(np.ones((S, 4, 64), np.float32))
+    w = _bits(np.ones((S, 4), np.float32))
+    pos = np.random.default_rng(17).permutation(S) if permute else None
+    note(f"index threshold trap unsampled={unsampled} permute={permute}")
+    got = gpu_index(q, k_idx, w, topk, q_pos=pos)
+    ref = O.index_topk(q, k_idx, w, pos, topk)
+    assert_idx_equal(f"idx trap {unsampled}", got, ref)
+    if unsampled == 125:   # ties at 4*125: pool 25 first, then the lowest unsampled ids
+        last = S - 1 if pos is None else int(np.argmax(pos))
+        assert got[last].tolist() == list(range(26)) + list(range(64, 102))
+
+
 # ---------------------------------------------------------------------------
 # attention: forward and backward
 
