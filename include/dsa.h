@@ -155,15 +155,17 @@ int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32
  * All sums are fp32; dq, dk and dv are rounded to bf16 (nearest even) and
  * overwritten completely (0 for keys no row attends).  dq is computed per
  * query row; dk and dv per pool of 4 keys, over the query rows whose key set
- * holds the pool, found by inverting idx in the workspace.  The order in
- * which a pool's rows are summed comes from device atomics and is not fixed.
+ * holds the pool, found by inverting idx in the workspace (counting per
+ * chunk of rows in LDS, no global atomics).  The order in which a pool's
+ * rows are summed follows LDS atomics and is not fixed from call to call.
  *
  *   q, out, dout [Sq, heads, head_dim] bf16   k, v [Sk, head_dim] bf16
  *   lse [Sq, heads] fp32 (from the forward)   idx, q_pos as in the forward
  *   dq [Sq, heads, head_dim] bf16             dk, dv [Sk, head_dim] bf16
  *   ws  workspace of ws_bytes >= dsa_sparse_attn_bwd_ws_bytes(...) bytes
- *       (Delta, per-pool offsets and the inverted lists: about
- *       4 * (Sq * (heads + topk + 1) + Sk / 4) bytes)
+ *       (Delta, per-pool offsets, the inverted lists and per-chunk pool
+ *       counts: about 4 * (Sq * (heads + topk + 1) + Sk / 4) bytes plus at
+ *       most 16 MiB)
  *
  * Supported: as the forward, and Sq * (topk + 1) < 2^31.  Returns 0 bytes
  * for arguments outside that.

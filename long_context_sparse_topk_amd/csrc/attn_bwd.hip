@@ -223,49 +223,143 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
 // inverse of the idx lists: for every pool, the query rows that attend it
 // (selected pools, plus the row's own incomplete pool)
 
+// Inverse of the idx lists: for every pool, the query rows whose key set
+// holds it, as one array `list` with the rows of pool p at
+// [end[p-1], end[p]).  The rows are split into chunks and the pools into
+// slices of kInvSlice; one workgroup per (chunk, slice) counts, and later
+// places, its chunk's entries of its slice with LDS atomics, so no global
+// atomics are needed:
+//   inv_count_kernel         cnt[c][p] = entries of pool p in chunk c
+//   inv_chunk_prefix_kernel  cnt[c][p] = entries of p in chunks before c; offs[p] = total
+//   scan kernels             offs[p] = end of p's rows (inclusive scan)
+//   inv_place_kernel         list[start(p) + cnt[c][p] + rank in chunk] = row
+// Within a (chunk, pool) the rows' order follows the LDS atomics.
 struct InvArgs {
   const int32_t* idx;
   const int32_t* q_pos;
   int64_t Sq, Sk;
   int topk;
-  int chunks;              // workgroups per row: ceil((topk + 1) / 256)
-  int32_t* offs;           // per pool: count, then (after the scan) start, then end
+  int64_t np;              // pools
+  int64_t chunk_rows;      // rows per chunk
+  int64_t chunks;
+  int nslices;
+  int32_t* cnt;            // [chunks][np]
+  int32_t* offs;           // [np]
   int32_t* list;
 };
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = v;
-}
+// Calls f(pool - p0, row) for every entry of rows [r0, r1) whose pool lies
+// in [p0, p1).  Entry j < topk of row r (position i, nc = floor((i+1)/4)
+// complete pools) is pool idx[r][j] if 0 <= idx[r][j] < nc; entry topk is
+// the row's own incomplete pool nc if (i+1) % 4 != 0.  The workgroup's 256 threads walk
+// the entries (row, j), j = 0..topk, in row-major order, kInvUnroll entries
+// per thread at a time; the loads use in-bounds clamped indices and are
+// issued unconditionally, so that they are in flight together.
+constexpr int kInvUnroll = 8;
 
-// Pool of entry j of row r (j == topk: the row's own incomplete pool), or -1.
-__device__ __forceinline__ int entry_pool(const InvArgs& a, int64_t r, int j) {
-  const int pos = clamp_pos(a.q_pos, r, a.Sk);
-  const int nc = (pos + 1) >> 2;
-  if (j < a.topk) {
-    const int p = a.idx[r * a.topk + j];
-    return (p >= 0 && p < nc) ? p : -1;
+template <bool kPos, typename F>
+__device__ __forceinline__ void for_entries(const InvArgs& a, int64_t r0, int64_t r1, int p0, int p1,
+                                            F&& f) {
+  const int per = a.topk + 1;
+  const int step_r = 256 / per, step_j = 256 % per;   // a stride of 256 entries
+  int64_t r = r0 + (int)threadIdx.x / per;
+  int j = (int)threadIdx.x % per;
+  while (r < r1) {
+    int64_t rr[kInvUnroll];
+    int jj[kInvUnroll], id[kInvUnroll], ps[kInvUnroll];
+#pragma unroll
+    for (int u = 0; u < kInvUnroll; ++u) {
+      rr[u] = r;
+      jj[u] = j;
+      const int64_t rc = r < r1 ? r : r1 - 1;
+      id[u] = a.idx[rc * a.topk + (j < a.topk ? j : a.topk - 1)];
+      ps[u] = kPos ? a.q_pos[rc] : (int)rc;
+      r += step_r;
+      j += step_j;
+      const bool wrap = j >= per;
+      j = wrap ? j - per : j;
+      r += wrap ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kInvUnroll; ++u) {
+      if (rr[u] >= r1) continue;
+      const int pos = kPos ? (ps[u] < 0 ? 0 : (ps[u] >= a.Sk ? (int)(a.Sk - 1) : ps[u])) : ps[u];
+      const int nc = (pos + 1) >> 2;
+      int p;
+      if (jj[u] < a.topk) p = (id[u] >= 0 && id[u] < nc) ? id[u] : -1;
+      else p = ((pos + 1) & 3) ? nc : -1;
+      if (p >= p0 && p < p1) f(p - p0, rr[u]);
+    }
   }
-  return ((pos + 1) & 3) ? nc : -1;
 }
 
-template <bool kScatter>
-__global__ __launch_bounds__(256) void pool_rows_kernel(InvArgs a) {
-  const int64_t r = blockIdx.x / a.chunks;
-  const int j = (int)(blockIdx.x % a.chunks) * 256 + (int)threadIdx.x;
-  if (r >= a.Sq || j > a.topk) return;
-  const int p = entry_pool(a, r, j);
-  if (p < 0) return;
-  if (kScatter) {
-    const int at = atomicAdd(&a.offs[p], 1);
-    a.list[at] = (int32_t)r;
-  } else {
-    atomicAdd(&a.offs[p], 1);
+template <typename F>
+__device__ __forceinline__ void for_chunk_entries(const InvArgs& a, int64_t r0, int64_t r1, int p0,
+                                                  int p1, F&& f) {
+  if (a.q_pos) for_entries<true>(a, r0, r1, p0, p1, f);
+  else for_entries<false>(a, r0, r1, p0, p1, f);
+}
+
+__global__ __launch_bounds__(256) void inv_count_kernel(InvArgs a) {
+  __shared__ int32_t h[kInvSlice];
+  const int64_t c = blockIdx.x / a.nslices;
+  const int p0 = (int)(blockIdx.x % a.nslices) * kInvSlice;
+  const int p1 = (int)min((int64_t)p0 + kInvSlice, a.np);
+  for (int i = threadIdx.x; i < kInvSlice; i += 256) h[i] = 0;
+  __syncthreads();
+  const int64_t r0 = c * a.chunk_rows;
+  for_chunk_entries(a, r0, min(r0 + a.chunk_rows, a.Sq), p0, p1, [&](int i, int64_t) { atomicAdd(&h[i], 1); });
+  __syncthreads();
+  int32_t* dst = a.cnt + c * a.np + p0;
+  for (int i = threadIdx.x; i < p1 - p0; i += 256) dst[i] = h[i];
+}
+
+// One thread per pool: per-chunk counts -> exclusive prefix over the
+// chunks; the pool's total to offs.
+__global__ __launch_bounds__(256) void inv_chunk_prefix_kernel(InvArgs a) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= a.np) return;
+  int32_t* col = a.cnt + p;
+  int s = 0;
+  int64_t c = 0;
+  for (; c + 8 <= a.chunks; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = col[(c + u) * a.np];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      col[(c + u) * a.np] = s;
+      s += v[u];
+    }
   }
+  for (; c < a.chunks; ++c) {
+    const int v = col[c * a.np];
+    col[c * a.np] = s;
+    s += v;
+  }
+  a.offs[p] = s;
 }
 
-// Exclusive scan of n counts in place, in blocks of kScanBlock: block sums,
-// a scan of the block sums (one workgroup), then each block's local scan.
+__global__ __launch_bounds__(256) void inv_place_kernel(InvArgs a) {
+  __shared__ int32_t h[kInvSlice];
+  const int64_t c = blockIdx.x / a.nslices;
+  const int p0 = (int)(blockIdx.x % a.nslices) * kInvSlice;
+  const int p1 = (int)min((int64_t)p0 + kInvSlice, a.np);
+  const int32_t* pre = a.cnt + c * a.np;
+  for (int i = threadIdx.x; i < p1 - p0; i += 256) {
+    const int p = p0 + i;
+    h[i] = (p > 0 ? a.offs[p - 1] : 0) + pre[p];   // start of p's rows + earlier chunks
+  }
+  __syncthreads();
+  const int64_t r0 = c * a.chunk_rows;
+  for_chunk_entries(a, r0, min(r0 + a.chunk_rows, a.Sq), p0, p1, [&](int i, int64_t r) {
+    a.list[atomicAdd(&h[i], 1)] = (int32_t)r;
+  });
+}
+
+// Inclusive scan of n counts in place, in blocks of kScanBlock: block sums,
+// an exclusive scan of the block sums (one workgroup), then each block's
+// local scan.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_w, int& total) {
   // 1024 threads: wave scans, then a scan of the 16 wave totals
   const int lane = lane_id(), w = threadIdx.x >> 6;
@@ -321,6 +415,7 @@ __global__ __launch_bounds__(1024) void scan_sums_kernel(int32_t* __restrict__ b
   }
 }
 
+// Writes the inclusive scan (each element: the sum up to and including it).
 __global__ __launch_bounds__(1024) void scan_apply_kernel(int32_t* __restrict__ c,
                                                           const int32_t* __restrict__ bsum, int64_t n) {
   __shared__ int lds_w[32];
@@ -336,8 +431,8 @@ __global__ __launch_bounds__(1024) void scan_apply_kernel(int32_t* __restrict__ 
   int ex = block_exclusive_scan(s, lds_w, total) + bsum[blockIdx.x];
 #pragma unroll
   for (int i = 0; i < kScanBlock / 1024; ++i) {
-    if (base + i < n) c[base + i] = ex;
     ex += v[i];
+    if (base + i < n) c[base + i] = ex;
   }
 }
 
@@ -534,22 +629,26 @@ hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s) {
   const int64_t nb = (np + kScanBlock - 1) / kScanBlock;
 
   // inverse of the idx lists
-  fill_i32_kernel<<<dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s>>>(offs, np, 0);
   InvArgs ia;
   ia.idx = x.idx;
   ia.q_pos = x.q_pos;
   ia.Sq = x.Sq;
   ia.Sk = x.Sk;
   ia.topk = x.topk;
-  ia.chunks = (x.topk + 1 + 255) / 256;
+  ia.np = np;
+  ia.chunk_rows = (x.Sq + bwd_chunks(x.Sq, x.Sk) - 1) / bwd_chunks(x.Sq, x.Sk);
+  ia.chunks = (x.Sq + ia.chunk_rows - 1) / ia.chunk_rows;   // <= bwd_chunks: fits the workspace
+  ia.nslices = (int)((np + kInvSlice - 1) / kInvSlice);
+  ia.cnt = reinterpret_cast<int32_t*>(ws + L.chunk_off);
   ia.offs = offs;
   ia.list = list;
-  const unsigned rb = (unsigned)(x.Sq * ia.chunks);
-  pool_rows_kernel<false><<<dim3(rb), dim3(256), 0, s>>>(ia);
+  const unsigned inv_blocks = (unsigned)(ia.chunks * ia.nslices);
+  inv_count_kernel<<<dim3(inv_blocks), dim3(256), 0, s>>>(ia);
+  inv_chunk_prefix_kernel<<<dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s>>>(ia);
   scan_block_sums_kernel<<<dim3((unsigned)nb), dim3(1024), 0, s>>>(offs, bsum, np);
   scan_sums_kernel<<<dim3(1), dim3(1024), 0, s>>>(bsum, nb);
   scan_apply_kernel<<<dim3((unsigned)nb), dim3(1024), 0, s>>>(offs, bsum, np);
-  pool_rows_kernel<true><<<dim3(rb), dim3(256), 0, s>>>(ia);
+  inv_place_kernel<<<dim3(inv_blocks), dim3(256), 0, s>>>(ia);
 
   // dq (and Delta)
   BwdArgs a;

@@ -101,8 +101,24 @@ constexpr int kScanBlock = 4096;
 
 inline int64_t bwd_pools(int64_t Sk) { return (Sk + 3) / 4; }
 
+// The inverse lists are built per (chunk of query rows, slice of pools): a
+// workgroup counts its chunk's entries of its slice in LDS.  Chunks hold at
+// least kInvRows rows; their number is capped so that the per-chunk counts
+// (chunks x pools int32) stay within kInvCounts.
+constexpr int kInvSlice = 16384;            // pools per slice (64 KiB of LDS counters)
+constexpr int kInvRows = 256;               // fewest rows per chunk
+constexpr int64_t kInvCounts = 1 << 22;     // most chunk counts kept (16 MiB)
+
+inline int64_t bwd_chunks(int64_t Sq, int64_t Sk) {
+  const int64_t np = bwd_pools(Sk);
+  int64_t c = (Sq + kInvRows - 1) / kInvRows;
+  const int64_t cap = kInvCounts / (np > 0 ? np : 1);
+  if (c > cap) c = cap;
+  return c > 0 ? c : 1;
+}
+
 struct BwdWorkspace {
-  size_t delta_off, count_off, bsum_off, list_off, total;
+  size_t delta_off, count_off, bsum_off, list_off, chunk_off, total;
 };
 
 inline BwdWorkspace bwd_ws_layout(int64_t Sq, int64_t Sk, int heads, int topk) {
@@ -113,7 +129,8 @@ inline BwdWorkspace bwd_ws_layout(int64_t Sq, int64_t Sk, int heads, int topk) {
   w.count_off = align256((size_t)Sq * heads * 16);
   w.bsum_off = w.count_off + align256((size_t)np * 4);
   w.list_off = w.bsum_off + align256((size_t)nb * 4);
-  w.total = w.list_off + align256((size_t)Sq * (topk + 1) * 4);
+  w.chunk_off = w.list_off + align256((size_t)Sq * (topk + 1) * 4);
+  w.total = w.chunk_off + align256((size_t)bwd_chunks(Sq, Sk) * np * 4);
   return w;
 }
 

@@ -47,7 +47,8 @@ def test_workspace_sizes():
     assert 0 < a < b < 2 * 2**30          # chunked indexer scratch stays below 2 GiB
     assert D.index_topk_ws_bytes(131072, 131072, 128) < 2**30
     assert D.lib().dsa_index_topk_ws_bytes(10, 10, 4, 64, 4, 0, 1) == 0
-    # Delta (Sq x heads), one offset per pool, the inverted lists (Sq x (topk + 1))
+    # Delta (Sq x heads), one offset per pool, the inverted lists (Sq x (topk + 1)) and per-chunk
+    # pool counts (at most 16 MiB)
     assert D.sparse_attn_bwd_ws_bytes(10, 1000, 4, 8) >= 4 * (10 * 4 + 250 + 10 * 9)
     assert D.sparse_attn_bwd_ws_bytes(131072, 131072, 4, 128) < 2**27
     assert D.lib().dsa_sparse_attn_bwd_ws_bytes(10, 1000, 4, 128, 0) == 0
