@@ -333,6 +333,45 @@ def test_full_size_pipeline_sampled(name):
         assert sdk < 1.0
 
 
+def test_backward_many_row_chunks_and_pool_slices():
+    # 10,000 query rows at scattered positions of a 524,291-key sequence: the
+    # inverse selection lists are built over 31 row chunks (the cap on chunk
+    # counters binds) and 9 pool slices, the last holding only the partial
+    # pool 131,072 (the own pool of the rows at the last 3 positions).  Every
+    # row selects 32 of 512 "hot" pools, so each hot pool's rows span every
+    # chunk.
+    Sk, Sq, H, topk = 524291, 10000, 2, 32
+    rng = np.random.default_rng([7, 11])
+    pos = rng.choice(np.arange(Sk // 2, Sk - 3), size=Sq - 3, replace=False)
+    pos = np.concatenate([pos, [Sk - 3, Sk - 2, Sk - 1]])
+    rng.shuffle(pos)
+    pos = pos.astype(np.int32)
+    hot = rng.choice(Sk // 32, size=512, replace=False)          # below every row's n_c
+    idx = np.sort(np.stack([rng.choice(hot, size=topk, replace=False) for _ in range(Sq)]),
+                  axis=1).astype(np.int32)
+    q = _bits(rng.standard_normal((Sq, H, 128)).astype(np.float32))
+    k = _bits(rng.standard_normal((Sk, 128)).astype(np.float32))
+    v = _bits(rng.standard_normal((Sk, 128)).astype(np.float32))
+    dout = _bits(rng.standard_normal((Sq, H, 128)).astype(np.float32))
+    note("backward: 31 row chunks x 9 pool slices")
+    tq, ti = dev_i32(pos), dev_i32(idx)
+    tqq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out, lse = D.sparse_attn_fwd(tqq, tk, tv, ti, q_pos=tq, scale=SCALE)
+    dq, dk, dv = D.sparse_attn_bwd(tqq, tk, tv, out, dev_bf16(dout), lse, ti, q_pos=tq, scale=SCALE)
+    torch.cuda.synchronize()
+    hot_keys = (4 * np.sort(hot)[[0, 100, 257, 511]][:, None] + np.arange(4)[None, :]).ravel()
+    keys = np.unique(np.concatenate([hot_keys, [Sk - 4, Sk - 3, Sk - 2, Sk - 1, 0],
+                                     rng.integers(0, Sk, 6)]))
+    rows = np.unique(np.concatenate([rng.integers(0, Sq, 40), np.nonzero(pos >= Sk - 3)[0]]))
+    dq_ref, dk_ref, dv_ref = O.sparse_attn_bwd(q, k, v, dout, idx, pos, SCALE, rows=rows, key_rows=keys)
+    sel = torch.from_numpy(rows).cuda()
+    ks = torch.from_numpy(keys).cuda()
+    assert_close("chunked dq", host_f64(dq[sel]), dq_ref)
+    assert_close("chunked dk", host_f64(dk[ks]), dk_ref)
+    assert_close("chunked dv", host_f64(dv[ks]), dv_ref)
+    assert np.abs(dk_ref[np.isin(keys, hot_keys)]).min() > 0   # the hot keys have many rows
+
+
 @pytest.mark.parametrize("name", ["s128k", "zigzag4"])
 def test_full_size_backward_sampled_keys(name):
     # dK/dV of sampled keys need every query that selected them: use a random
