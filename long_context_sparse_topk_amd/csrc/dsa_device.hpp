@@ -23,16 +23,8 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// Two values at once by the hardware pack conversion (v_cvt_pk_bf16_f32):
-// the same rounding (nearest even), one instruction, no branch.
+// Two floats to two bf16 values (round to nearest even) by the hardware
+// pack conversion (v_cvt_pk_bf16_f32).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -131,11 +123,6 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
   for (int o = 32; o >= 1; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o, kWave);
   return v;
@@ -143,11 +130,6 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 
 __device__ __forceinline__ uint32_t wave_and(uint32_t v) {
   for (int o = 32; o >= 1; o >>= 1) v &= (uint32_t)__shfl_xor((int)v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 
