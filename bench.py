@@ -264,8 +264,12 @@ def main():
     secondary = None
     if args.secondary and args.secondary != wl.name:
         sw = syn.WORKLOADS[args.secondary]
+        # device memory of the secondary workload alone: its inputs, outputs and workspaces
+        base_mem = torch.cuda.memory_allocated(device)
+        torch.cuda.reset_peak_memory_stats(device)
         sl = Layer(sw, device)
         swall, savg = run(sl, args.steps, args.warmup)
+        peak_mem = torch.cuda.max_memory_allocated(device) - base_mem
         sws = work(sw)
         secondary = {"workload": sw.name, "tokens_per_s": round(sw.sq * args.steps / swall, 1),
                      "ms_per_step": round(swall / args.steps * 1e3, 3),
@@ -275,6 +279,10 @@ def main():
                      "fwd_gather_GBps": round(sws["fwd_bytes"] / savg["fwd"] / 1e9, 1)}
         if sw.backward:
             secondary["bwd_GBps"] = round(sws["bwd_bytes"] / savg["bwd"] / 1e9, 1)
+        secondary["peak_mem_bytes"] = int(peak_mem)
+        secondary["index_ws_bytes"] = int(sl.ws_idx.numel())
+        if sw.backward:
+            secondary["bwd_ws_bytes"] = int(sl.ws_bwd.numel())
         del sl
 
     cpu = None
