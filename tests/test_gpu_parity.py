@@ -211,8 +211,9 @@ def _check_attn(tag, got, d, idx, q_pos, bwd=True):
 
 
 @pytest.mark.parametrize("S,H,topk", [(2048, 4, 32), (4096, 16, 512), (1031, 3, 16), (9, 1, 1),
-                                      (2053, 16, 128)])
+                                      (2053, 16, 128), (8400, 2, 2048)])
 def test_pipeline_small(S, H, topk):
+    # (8400, 2, 2048): the largest k; the last rows attend 4k + 3 = 8195 keys
     note(f"pipeline small S={S} H={H} topk={topk}")
     q_idx, k_idx, w_idx = _int_inputs(S, S, seed=S + H)
     idx = gpu_index(q_idx, k_idx, w_idx, topk)
