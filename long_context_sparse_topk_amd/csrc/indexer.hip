@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       const int nt = first < ntp ? (ntp - first + step - 1) / step : 0;
       dma(first < ntp ? first : 0, 0);
       if (nt > 1) dma(first + step, 1);
-      int buf = 0;
+      int buf = 0, lbuf = 2;  // buffer of tile i, and of tile i+2 ((buf + 2) mod kRing)
       for (int i = 0; i < nt; ++i) {
         const int pt0 = (first + i * step) * kPT;
         if (i + 1 < nt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt2);
@@ -432,8 +432,9 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         lds_barrier();
         const u32x4_t* kb = lds_k[buf];
         before_load(i);
-        if (i + 2 < nt) dma(first + (i + 2) * step, buf == 0 ? 2 : buf - 1);
+        if (i + 2 < nt) dma(first + (i + 2) * step, lbuf);
         buf = buf == kRing - 1 ? 0 : buf + 1;
+        lbuf = lbuf == kRing - 1 ? 0 : lbuf + 1;
 
         // 16 output blocks of 16 (query x head) rows x 16 pools
         f32x4_t acc[4][4];
@@ -506,21 +507,30 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int j = 0; j < kSampleKeep; ++j) best[rb][j] = NEG_INF;
+      // Per tile and query the lane's 4 new scores are sorted (5 exchanges),
+      // merged into the 8 kept ones by taking the larger of kept[4+j] and
+      // new[3-j] (the top 8 of the union, in bitonic order), and the 8 are
+      // sorted again by a bitonic half-cleaner network (3 x 4 exchanges).
       stream(0, kSampleStride, [](int) {}, [&](float (&sc)[4][4], int) {
+        auto cx = [](float& hi, float& lo) {
+          const float h = fmaxf(hi, lo);
+          lo = fminf(hi, lo);
+          hi = h;
+        };
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
+          float n0 = sc[rb][0], n1 = sc[rb][1], n2 = sc[rb][2], n3 = sc[rb][3];
+          cx(n0, n1); cx(n2, n3); cx(n0, n2); cx(n1, n3); cx(n1, n2);
+          float* b = best[rb];
+          b[4] = fmaxf(b[4], n3);
+          b[5] = fmaxf(b[5], n2);
+          b[6] = fmaxf(b[6], n1);
+          b[7] = fmaxf(b[7], n0);
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            float x = sc[rb][cb];
-            if (ballot(x > best[rb][kSampleKeep - 1])) {
+          for (int d = 4; d >= 1; d >>= 1)
 #pragma unroll
-              for (int j = 0; j < kSampleKeep; ++j) {
-                const float hi = fmaxf(best[rb][j], x);
-                x = fminf(best[rb][j], x);
-                best[rb][j] = hi;
-              }
-            }
-          }
+            for (int j = 0; j < kSampleKeep; ++j)
+              if ((j & d) == 0) cx(b[j], b[j + d]);
         }
       });
       // r-th best of the 16 lanes x kSampleKeep kept scores of each query:
@@ -633,13 +643,16 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
             // all 4 stages of a wave are flushed together, when one of them
             // could not take another tile's worth (4 x 64 entries), and every
             // kFlushPeriod tiles (the same tiles in every wave).
-            bool full = false;
+            // scalar-only tests: full = some count > kStage - 256 (the sign
+            // bit of count - (kStage - 255) is clear), fl = counts > 0
+            int neg = -1;
             uint32_t fl = 0;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-              full |= nst[rb] > kStage - 4 * kWave;
-              fl |= nst[rb] > 0 ? 1u << rb : 0u;
+              neg &= nst[rb] - (kStage - 4 * kWave + 1);
+              fl |= ((uint32_t)(-nst[rb]) >> 31) << rb;
             }
+            const bool full = neg >= 0;
             if (!(full || (i > 0 && (i % kFlushPeriod) == 0)) || fl == 0) return;
             flush(fl);
             bool fenced = false;
@@ -665,12 +678,19 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
             }
           },
           [&](float (&sc)[4][4], int pt0) {
+            // all 16 ballots come before the first branch on one of them, so
+            // no branch waits on a compare issued just before it
+            uint64_t MM[4][4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+              for (int cb = 0; cb < 4; ++cb) MM[rb][cb] = ballot(sc[rb][cb] > tau[rb]);
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
               for (int cb = 0; cb < 4; ++cb) {
                 const bool keep = sc[rb][cb] > tau[rb];
-                const uint64_t M = ballot(keep);
+                const uint64_t M = MM[rb][cb];
                 if (M) {
                   if (keep) {
                     const int slot = nst[rb] + mbcnt(M);
