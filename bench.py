@@ -3,10 +3,12 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload s1m] [--secondary s128k]
 
 A step is one pass of the layer's hot path over one batch of synthetic input
-already resident in HBM: indexer + fused top-k, sparse attention forward, and
-the backward for workloads that train (s128k, zigzag4).  Prints one JSON line:
-tokens/s of the primary workload, the roofline of its dominant kernel
-(per-launch durations from HIP events on the launch stream), the CPU oracle
+already resident in HBM: indexer + fused top-k and sparse attention forward
+(one pipelined call that overlaps the two over query chunks on two streams),
+and the backward for workloads that train (s128k, zigzag4).  Prints one JSON
+line: tokens/s of the primary workload over the timed steps, the roofline of
+its dominant kernel (per-launch durations from HIP events on the launch stream,
+in a pass of the separate entry points after the timed steps), the CPU oracle
 timed on a bounded sample of the same workload, and the secondary workload's
 tokens/s.
 """
@@ -110,20 +112,40 @@ class Layer:
         torch.cuda.synchronize()
 
     def step(self, ev=None):
+        """One step: indexer + top-k and forward pipelined over query chunks (one call), then
+        the backward for training workloads.  ev: events around the two parts."""
         t, wl = self.t, self.wl
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
+        D.index_attn_fwd(t["q_idx"], t["k_idx"], t["w_idx"], t["q"], t["k"], t["v"], topk=wl.topk,
+                         q_chunk=wl.q_chunk, q_pos=self.q_pos, scale=SCALE, idx=self.idx, out=self.out,
+                         lse=self.lse, ws=self.ws_idx)
+        rec(1)
+        if wl.backward:
+            self.backward()
+            rec(2)
+
+    def backward(self):
+        t, wl = self.t, self.wl
+        D.sparse_attn_bwd(t["q"], t["k"], t["v"], self.out, t["dout"], self.lse, self.idx,
+                          q_pos=self.q_pos, scale=SCALE, ws=self.ws_bwd, dq=self.dq, dk=self.dk,
+                          dv=self.dv)
+
+    def kernels(self, ev):
+        """The same work as separate entry-point calls, one after the other on the current
+        stream (the stream every kernel of these calls is launched on), with events around
+        each: the per-launch durations of the kernels in isolation."""
+        t, wl = self.t, self.wl
+        ev[0].record()
         D.index_topk(t["q_idx"], t["k_idx"], t["w_idx"], topk=wl.topk, q_chunk=wl.q_chunk,
                      q_pos=self.q_pos, out=self.idx, ws=self.ws_idx)
-        rec(1)
+        ev[1].record()
         D.sparse_attn_fwd(t["q"], t["k"], t["v"], self.idx, q_pos=self.q_pos, scale=SCALE,
                           out=self.out, lse=self.lse)
-        rec(2)
+        ev[2].record()
         if wl.backward:
-            D.sparse_attn_bwd(t["q"], t["k"], t["v"], self.out, t["dout"], self.lse, self.idx,
-                              q_pos=self.q_pos, scale=SCALE, ws=self.ws_bwd, dq=self.dq, dk=self.dk,
-                              dv=self.dv)
-            rec(3)
+            self.backward()
+            ev[3].record()
 
 
 def parts_names(parts):
@@ -138,25 +160,35 @@ def parts_names(parts):
 
 
 def run(layer: Layer, steps: int, warmup: int):
+    """Time `steps` pipelined steps (wall clock between synchronisations), then the same
+    number of passes of the separate calls for per-kernel durations."""
     for _ in range(warmup):
         layer.step()
     torch.cuda.synchronize()
-    n_ev = 4 if layer.wl.backward else 3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    bw = layer.wl.backward
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3 if bw else 2)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        layer.step(evs[s])
+        layer.step(sev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {"index": [], "fwd": [], "bwd": []}
-    for e in evs:
-        per["index"].append(e[0].elapsed_time(e[1]) / 1e3)
-        per["fwd"].append(e[1].elapsed_time(e[2]) / 1e3)
-        if layer.wl.backward:
-            per["bwd"].append(e[2].elapsed_time(e[3]) / 1e3)
-    avg = {k: float(np.mean(v)) for k, v in per.items() if v}
-    return wall, avg
+    step_parts = {"index_fwd_pipelined": [e[0].elapsed_time(e[1]) / 1e3 for e in sev]}
+    if bw:
+        step_parts["bwd"] = [e[1].elapsed_time(e[2]) / 1e3 for e in sev]
+
+    layer.kernels([torch.cuda.Event(enable_timing=True) for _ in range(4)])   # warm the pass
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(4 if bw else 3)] for _ in range(steps)]
+    for s in range(steps):
+        layer.kernels(kev[s])
+    torch.cuda.synchronize()
+    per = {"index": [e[0].elapsed_time(e[1]) / 1e3 for e in kev],
+           "fwd": [e[1].elapsed_time(e[2]) / 1e3 for e in kev]}
+    if bw:
+        per["bwd"] = [e[2].elapsed_time(e[3]) / 1e3 for e in kev]
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    avg_step = {k: float(np.mean(v)) for k, v in step_parts.items()}
+    return wall, avg, avg_step
 
 
 def source_hash(rel: str) -> str:
@@ -237,7 +269,7 @@ def main():
     wl = syn.WORKLOADS[args.workload]
     layer = Layer(wl, device)
     log(f"{wl.name}: warmup {args.warmup}, timed {args.steps}")
-    wall, avg = run(layer, args.steps, args.warmup)
+    wall, avg, avg_step = run(layer, args.steps, args.warmup)
     w = work(wl)
     step_s = wall / args.steps
     value = wl.sq / step_s
@@ -268,13 +300,15 @@ def main():
         base_mem = torch.cuda.memory_allocated(device)
         torch.cuda.reset_peak_memory_stats(device)
         sl = Layer(sw, device)
-        swall, savg = run(sl, args.steps, args.warmup)
+        swall, savg, sstep = run(sl, args.steps, args.warmup)
         peak_mem = torch.cuda.max_memory_allocated(device) - base_mem
         sws = work(sw)
         secondary = {"workload": sw.name, "tokens_per_s": round(sw.sq * args.steps / swall, 1),
                      "ms_per_step": round(swall / args.steps * 1e3, 3),
                      "pass": "index+fwd+bwd" if sw.backward else "index+fwd",
                      "ms": {k: round(v * 1e3, 3) for k, v in savg.items()},
+                     "step_ms": {k: round(v * 1e3, 3) for k, v in sstep.items()},
+                     "separate_calls_ms_per_step": round(sum(savg.values()) * 1e3, 3),
                      "index_mfma_frac": round(sws["index_flop"] / savg["index"] / BF16_PEAK, 4),
                      "fwd_gather_GBps": round(sws["fwd_bytes"] / savg["fwd"] / 1e9, 1)}
         if sw.backward:
@@ -309,6 +343,10 @@ def main():
                    "pass": "index+fwd+bwd" if wl.backward else "index+fwd", "parallelism": "single-gpu"},
         "roofline": roofline,
         "kernels": kernels,
+        # the step's parts as timed (indexer and forward pipelined in one call), and the same
+        # work as separate calls one after the other (the per-kernel durations above)
+        "step_ms": {k: round(v * 1e3, 3) for k, v in avg_step.items()},
+        "separate_calls_ms_per_step": round(sum(avg.values()) * 1e3, 3),
         "index_mfma_frac": round(w["index_flop"] / avg["index"] / BF16_PEAK, 4),
         "fwd_gather_GBps": round(w["fwd_bytes"] / avg["fwd"] / 1e9, 1),
         "cpu_baseline": cpu,

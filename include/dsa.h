@@ -145,6 +145,45 @@ int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32
                         void* out, float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Indexer + top-k followed by the sparse attention forward, pipelined.
+ *
+ * Computes exactly what dsa_index_topk followed by dsa_sparse_attn_fwd on its
+ * idx_out compute (the same kernels, so idx_out, out and lse are equal bit
+ * for bit), with the work split into contiguous chunks of query rows: the
+ * indexer of chunk c+1 runs on `stream` while the forward of chunk c runs on
+ * `aux_stream`.  The indexer is bound by matrix and vector issue, the forward
+ * by the memory fabric, so the two overlap on the CUs.  The pages score the
+ * indexer in query chunks to bound its memory (SkyRL news item, section
+ * "四块优化 1. DSA 真稀疏"); here the chunks exist to overlap the two stages.
+ *
+ * Arguments are those of the two calls: the indexer's (q_idx, k_idx, w_idx,
+ * idx_heads, idx_dim, q_chunk, ws, ws_bytes >= dsa_index_attn_fwd_ws_bytes())
+ * and the forward's (q, k, v, heads, head_dim, scale, out, lse); q_pos, Sq,
+ * Sk, pool and topk are shared, idx_out receives the selection.  Every
+ * supported-shape rule of both calls applies.
+ *
+ * Streams: work is enqueued on `stream` and `aux_stream` (which must belong
+ * to the same device), and before returning the call makes `stream` wait
+ * for everything it enqueued on `aux_stream`: the caller orders later work,
+ * or synchronises, on `stream` alone.  The forward of a chunk starts after
+ * that chunk's indexer on `stream`, so it also sees all earlier work of
+ * `stream`; earlier work of `aux_stream` stays ordered before it.  With
+ * aux_stream == stream the two stages run one after the other on `stream`.
+ * The call creates its events (one per chunk, at most 7) and destroys them
+ * before returning; the runtime releases each once it has completed.
+ * Chunks: about one per 2^17 query rows, at most 6, of equal indexer work.
+ */
+size_t dsa_index_attn_fwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim,
+                                   int32_t pool, int32_t topk, int32_t q_chunk);
+
+int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx, const void* q,
+                       const void* k, const void* v, const int32_t* q_pos, int64_t Sq,
+                       int64_t Sk, int32_t idx_heads, int32_t idx_dim, int32_t heads,
+                       int32_t head_dim, int32_t pool, int32_t topk, int32_t q_chunk,
+                       float scale, int32_t* idx_out, void* out, float* lse, void* ws,
+                       size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream);
+
+/* ---------------------------------------------------------------------------
  * Sparse attention backward.
  *
  * Gradients of L = sum(dout * O) for the forward above, with

@@ -8,6 +8,7 @@ built, importing works but every call raises DsaLibraryMissing.
     idx = index_topk(q_idx, k_idx, w_idx, topk=512, q_chunk=256, q_pos=None)
     out, lse = sparse_attn_fwd(q, k, v, idx, q_pos=None, scale=None)
     dq, dk, dv = sparse_attn_bwd(q, k, v, out, dout, lse, idx, q_pos=None, scale=None)
+    idx, out, lse = index_attn_fwd(q_idx, k_idx, w_idx, q, k, v, topk=512)  # pipelined
 
 Shapes: q_idx [Sq, 4, 64], k_idx [Sk, 64], w_idx [Sq, 4] (bf16); q [Sq, H, 128],
 k, v [Sk, 128] (bf16); idx [Sq, topk] int32; q_pos [Sq] int32 or None.
@@ -41,6 +42,9 @@ SIGNATURES = {
                                       _P, _P, _SZ, _P]),
     "dsa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
                                            _F, _P, _P, _P]),
+    "dsa_index_attn_fwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32, _I32]),
+    "dsa_index_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32,
+                                          _I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _SZ, _P, _P]),
     "dsa_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
     "dsa_sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32,
                                            _I32, _I32, _F, _P, _P, _P, _P, _SZ, _P]),
@@ -175,6 +179,59 @@ def sparse_attn_fwd(q, k, v, idx, *, q_pos=None, scale: float | None = None, out
                                idx.shape[1], scale, _ptr(out), _ptr(lse), _stream(dev))
     _check("dsa_sparse_attn_fwd", st)
     return out, lse
+
+
+_aux_streams = {}
+
+
+def _aux_stream(dev):
+    """A second stream of the device (default priority) for the pipelined forward."""
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key not in _aux_streams:
+        _aux_streams[key] = torch.cuda.Stream(device=dev)
+    return _aux_streams[key]
+
+
+def index_attn_fwd(q_idx, k_idx, w_idx, q, k, v, *, topk: int, q_chunk: int = 256, q_pos=None,
+                   scale: float | None = None, idx=None, out=None, lse=None, ws=None,
+                   aux_stream=None):
+    """index_topk then sparse_attn_fwd, pipelined over query chunks on two streams.
+
+    Returns (idx [Sq, topk] int32, out [Sq, H, 128] bf16, lse [Sq, H] fp32), equal bit for
+    bit to the two separate calls.  The current stream waits for all of the work on return.
+    """
+    L = lib()
+    dev = q_idx.device
+    _want(q_idx, "q_idx", torch.bfloat16, 3, dev)
+    _want(k_idx, "k_idx", torch.bfloat16, 2, dev)
+    _want(w_idx, "w_idx", torch.bfloat16, 2, dev)
+    _want(q, "q", torch.bfloat16, 3, dev)
+    _want(k, "k", torch.bfloat16, 2, dev)
+    _want(v, "v", torch.bfloat16, 2, dev)
+    Sq, HI, DI = q_idx.shape
+    Sk = k_idx.shape[0]
+    H, D = q.shape[1], q.shape[2]
+    if k_idx.shape[1] != DI or tuple(w_idx.shape) != (Sq, HI):
+        raise ValueError("indexer shapes disagree")
+    if q.shape[0] != Sq or tuple(v.shape) != tuple(k.shape) or k.shape[0] != Sk:
+        raise ValueError("attention shapes disagree")
+    q_pos = _positions(q_pos, Sq, dev)
+    scale = default_scale(D) if scale is None else float(scale)
+    idx = torch.empty((Sq, topk), dtype=torch.int32, device=dev) if idx is None else idx
+    _want(idx, "idx", torch.int32, 2, dev)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Sq, H), dtype=torch.float32, device=dev) if lse is None else lse
+    need = int(L.dsa_index_attn_fwd_ws_bytes(Sq, Sk, HI, DI, POOL, topk, q_chunk))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    aux = _aux_stream(dev) if aux_stream is None else aux_stream
+    st = L.dsa_index_attn_fwd(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(q_pos), Sq, Sk, HI, DI, H, D, POOL, topk, q_chunk, scale,
+                              _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(dev),
+                              ctypes.c_void_p(aux.cuda_stream))
+    _check("dsa_index_attn_fwd", st)
+    return idx, out, lse
 
 
 def sparse_attn_bwd(q, k, v, out, dout, lse, idx, *, q_pos=None, scale: float | None = None,

@@ -32,6 +32,7 @@ struct FwdArgs {
   const uint16_t* v;
   const int32_t* idx;
   const int32_t* q_pos;
+  int64_t q_base;  // position of row 0 when q_pos is NULL
   int64_t Sq, Sk;
   int H, topk;
   float scale_log2;
@@ -69,11 +70,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   const int c16 = lane & 15;
   const float NEG_INF = -__builtin_huge_valf();
 
-  int64_t pos64 = r;
-  if (a.q_pos) {
-    pos64 = a.q_pos[r];
-    pos64 = pos64 < 0 ? 0 : (pos64 >= a.Sk ? a.Sk - 1 : pos64);
-  }
+  int64_t pos64 = a.q_pos ? (int64_t)a.q_pos[r] : a.q_base + r;
+  pos64 = pos64 < 0 ? 0 : (pos64 >= a.Sk ? a.Sk - 1 : pos64);
   const int pos = (int)pos64;
   const int nc = (pos + 1) >> 2;
   const int part = (pos + 1) & 3;
@@ -109,8 +107,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
 
-    // K rows -> A operands; V rows -> LDS (same lane pattern)
+    // K rows -> A operands, V rows -> registers: all 16 loads of the tile are
+    // issued before any is waited on, so the tile costs one memory round trip
     bf16x8_t KA[2][4];
+    u32x4_t VR[2][4];
+    uint16_t* vdst[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int2 in = info[4 * kb + (c16 >> 2)];
@@ -118,14 +119,18 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
       const int64_t key = off < in.y ? in.x + off : pos;
       const uint16_t* ks_src = a.k + key * kD + 8 * g;
       const uint16_t* vs_src = a.v + key * kD + 8 * g;
-      uint16_t* vdst = vt + (16 * kb + c16) * kVStride + 8 * g;
+      vdst[kb] = vt + (16 * kb + c16) * kVStride + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         KA[kb][ks] = load_bf16x8(ks_src + 32 * ks);
-        *reinterpret_cast<u32x4_t*>(vdst + 32 * ks) =
-            *reinterpret_cast<const u32x4_t*>(vs_src + 32 * ks);
+        VR[kb][ks] = *reinterpret_cast<const u32x4_t*>(vs_src + 32 * ks);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4_t*>(vdst[kb] + 32 * ks) = VR[kb][ks];
 
     f32x4_t S[2];
 #pragma unroll
@@ -214,6 +219,7 @@ hipError_t launch_attn_fwd(const AttnArgs& x, hipStream_t s) {
   a.v = x.v;
   a.idx = x.idx;
   a.q_pos = x.q_pos;
+  a.q_base = x.q_base;
   a.Sq = x.Sq;
   a.Sk = x.Sk;
   a.H = x.heads;

@@ -69,6 +69,43 @@ int hip_status(hipError_t e, const char* what) {
   return fail(DSA_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
 }
 
+int check_index_shape(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim, int32_t pool,
+                      int32_t topk, int32_t q_chunk, const int32_t* q_pos, size_t ws_bytes) {
+  int st = check_seq(Sq, Sk, q_pos);
+  if (st) return st;
+  if (idx_dim != 64) return fail(DSA_UNSUPPORTED_SHAPE, "idx_dim=%d (supported: 64)", idx_dim);
+  if (idx_heads < 1 || idx_heads > 4)
+    return fail(DSA_UNSUPPORTED_SHAPE, "idx_heads=%d (supported: 1..4)", idx_heads);
+  if (pool != 4) return fail(DSA_UNSUPPORTED_SHAPE, "pool=%d (supported: 4)", pool);
+  if (topk < 1 || topk > dsa::kMaxTopk)
+    return fail(DSA_UNSUPPORTED_SHAPE, "topk=%d (supported: 1..%d)", topk, dsa::kMaxTopk);
+  if (q_chunk < 1) return fail(DSA_INVALID_ARG, "q_chunk=%d must be >= 1", q_chunk);
+  const size_t need = dsa::index_ws_layout(Sq, Sk, topk).total;
+  if (ws_bytes < need)
+    return fail(DSA_WORKSPACE_TOO_SMALL, "ws_bytes=%zu < %zu", ws_bytes, need);
+  return DSA_OK;
+}
+
+// Query chunks of the pipelined indexer + forward: about one per 2^17 query
+// rows, at most kPipeChunks.  Row r at position r costs the indexer about r
+// pool scores, so boundary c sits at Sq * sqrt(c / n) (equal indexer work per
+// chunk), on a multiple of the indexer's 64-query tile.
+constexpr int kPipeChunks = 6;
+constexpr int64_t kPipeRowsPerChunk = (int64_t)1 << 17;
+
+int pipe_chunks(int64_t Sq) {
+  const int64_t n = Sq / kPipeRowsPerChunk;
+  return n < 1 ? 1 : (n > kPipeChunks ? kPipeChunks : (int)n);
+}
+
+int64_t pipe_bound(int64_t Sq, int c, int n) {
+  if (c <= 0) return 0;
+  if (c >= n) return Sq;
+  const double x = (double)Sq * std::sqrt((double)c / (double)n);
+  int64_t b = (int64_t)std::llround(x / dsa::kIndexQueryTile) * dsa::kIndexQueryTile;
+  return b < 0 ? 0 : (b > Sq ? Sq : b);
+}
+
 }  // namespace
 
 DSA_EXPORT int dsa_version(void) { return 100; }
@@ -107,20 +144,11 @@ DSA_EXPORT int dsa_index_topk(const void* q_idx, const void* k_idx, const void* 
   if ((st = check_ptr(w_idx, "w_idx", 2))) return st;
   if ((st = check_ptr(idx_out, "idx_out", 4))) return st;
   if ((st = check_ptr(ws, "ws", 256))) return st;
-  if ((st = check_seq(Sq, Sk, q_pos))) return st;
-  if (idx_dim != 64) return fail(DSA_UNSUPPORTED_SHAPE, "idx_dim=%d (supported: 64)", idx_dim);
-  if (idx_heads < 1 || idx_heads > 4)
-    return fail(DSA_UNSUPPORTED_SHAPE, "idx_heads=%d (supported: 1..4)", idx_heads);
-  if (pool != 4) return fail(DSA_UNSUPPORTED_SHAPE, "pool=%d (supported: 4)", pool);
-  if (topk < 1 || topk > dsa::kMaxTopk)
-    return fail(DSA_UNSUPPORTED_SHAPE, "topk=%d (supported: 1..%d)", topk, dsa::kMaxTopk);
-  if (q_chunk < 1) return fail(DSA_INVALID_ARG, "q_chunk=%d must be >= 1", q_chunk);
-  const size_t need = dsa::index_ws_layout(Sq, Sk, topk).total;
-  if (ws_bytes < need)
-    return fail(DSA_WORKSPACE_TOO_SMALL, "ws_bytes=%zu < %zu", ws_bytes, need);
+  if ((st = check_index_shape(Sq, Sk, idx_heads, idx_dim, pool, topk, q_chunk, q_pos, ws_bytes)))
+    return st;
 
   (void)hipGetLastError();
-  dsa::IndexArgs a;
+  dsa::IndexArgs a{};
   a.q_idx = static_cast<const uint16_t*>(q_idx);
   a.k_idx = static_cast<const uint16_t*>(k_idx);
   a.w_idx = static_cast<const uint16_t*>(w_idx);
@@ -164,6 +192,119 @@ DSA_EXPORT int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, 
   a.out = static_cast<uint16_t*>(out);
   a.lse_out = lse;
   return hip_status(dsa::launch_attn_fwd(a, stream), "dsa_sparse_attn_fwd launch");
+}
+
+// Indexer + top-k and the sparse attention forward over query chunks on two
+// streams: the indexer of chunk c+1 runs on `stream` while the forward of
+// chunk c runs on `aux_stream`.  The indexer is bound by MFMA and VALU issue,
+// the forward by the memory fabric, so the two share the CUs: the indexer of
+// every chunk after the first keeps one workgroup per CU, which leaves each
+// CU the LDS and registers for forward waves beside it.  Every chunk runs the
+// same kernels on its rows, so the results equal the two separate calls bit
+// for bit.
+DSA_EXPORT size_t dsa_index_attn_fwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t idx_heads,
+                                              int32_t idx_dim, int32_t pool, int32_t topk,
+                                              int32_t q_chunk) {
+  return dsa_index_topk_ws_bytes(Sq, Sk, idx_heads, idx_dim, pool, topk, q_chunk);
+}
+
+DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx,
+                                  const void* q, const void* k, const void* v,
+                                  const int32_t* q_pos, int64_t Sq, int64_t Sk,
+                                  int32_t idx_heads, int32_t idx_dim, int32_t heads,
+                                  int32_t head_dim, int32_t pool, int32_t topk, int32_t q_chunk,
+                                  float scale, int32_t* idx_out, void* out, float* lse, void* ws,
+                                  size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream) {
+  g_err[0] = '\0';
+  int st;
+  if ((st = check_ptr(q_idx, "q_idx", 16))) return st;
+  if ((st = check_ptr(k_idx, "k_idx", 16))) return st;
+  if ((st = check_ptr(w_idx, "w_idx", 2))) return st;
+  if ((st = check_ptr(q, "q", 16))) return st;
+  if ((st = check_ptr(k, "k", 16))) return st;
+  if ((st = check_ptr(v, "v", 16))) return st;
+  if ((st = check_ptr(idx_out, "idx_out", 4))) return st;
+  if ((st = check_ptr(out, "out", 16))) return st;
+  if ((st = check_ptr(lse, "lse", 4))) return st;
+  if ((st = check_ptr(ws, "ws", 256))) return st;
+  if ((st = check_index_shape(Sq, Sk, idx_heads, idx_dim, pool, topk, q_chunk, q_pos, ws_bytes)))
+    return st;
+  if ((st = check_attn_shape(Sq, Sk, heads, head_dim, pool, topk, scale, q_pos))) return st;
+
+  const int n = aux_stream == stream ? 1 : pipe_chunks(Sq);
+  // events: one per chunk (indexer done) and one for the forward stream's end
+  hipEvent_t ev[kPipeChunks + 1] = {};
+  if (n > 1) {
+    for (int c = 0; c <= n; ++c) {
+      const hipError_t e = hipEventCreateWithFlags(&ev[c], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        for (int j = 0; j < c; ++j) (void)hipEventDestroy(ev[j]);
+        (void)hipGetLastError();
+        return hip_status(e, "dsa_index_attn_fwd: hipEventCreateWithFlags");
+      }
+    }
+  }
+  (void)hipGetLastError();
+  hipError_t err = hipSuccess;
+  auto note = [&](hipError_t e) {
+    if (err == hipSuccess && e != hipSuccess) err = e;
+  };
+  const auto* qi = static_cast<const uint16_t*>(q_idx);
+  const auto* wi = static_cast<const uint16_t*>(w_idx);
+  const auto* qq = static_cast<const uint16_t*>(q);
+  auto* oo = static_cast<uint16_t*>(out);
+  bool pooled = false;  // the workspace holds the pooled keys (chunks run in order on `stream`)
+  for (int c = 0; c < n && err == hipSuccess; ++c) {
+    const int64_t r0 = pipe_bound(Sq, c, n), r1 = pipe_bound(Sq, c + 1, n);
+    if (r1 <= r0) continue;
+    dsa::IndexArgs ia{};
+    ia.q_idx = qi + r0 * idx_heads * idx_dim;
+    ia.k_idx = static_cast<const uint16_t*>(k_idx);
+    ia.w_idx = wi + r0 * idx_heads;
+    ia.q_pos = q_pos ? q_pos + r0 : nullptr;
+    ia.q_base = q_pos ? 0 : r0;
+    ia.Sq = r1 - r0;
+    ia.Sk = Sk;
+    ia.heads = idx_heads;
+    ia.topk = topk;
+    ia.q_chunk = q_chunk;
+    ia.idx_out = idx_out + r0 * topk;
+    ia.ws = ws;
+    ia.max_per_cu = pooled ? 1 : 0;   // the first chunk has the GPU to itself
+    ia.pooled = pooled;
+    note(dsa::launch_index_topk(ia, stream));
+    pooled = true;
+    hipStream_t fs = stream;
+    if (n > 1) {
+      note(hipEventRecord(ev[c], stream));
+      note(hipStreamWaitEvent(aux_stream, ev[c], 0));
+      fs = aux_stream;
+    }
+    dsa::AttnArgs fa{};
+    fa.q = qq + r0 * heads * head_dim;
+    fa.k = static_cast<const uint16_t*>(k);
+    fa.v = static_cast<const uint16_t*>(v);
+    fa.idx = idx_out + r0 * topk;
+    fa.q_pos = q_pos ? q_pos + r0 : nullptr;
+    fa.q_base = q_pos ? 0 : r0;
+    fa.Sq = r1 - r0;
+    fa.Sk = Sk;
+    fa.heads = heads;
+    fa.topk = topk;
+    fa.scale = scale;
+    fa.out = oo + r0 * heads * head_dim;
+    fa.lse_out = lse + r0 * heads;
+    note(dsa::launch_attn_fwd(fa, fs));
+  }
+  if (n > 1) {
+    // `stream` waits for the last forward chunk, so the caller can wait on it alone
+    note(hipEventRecord(ev[n], aux_stream));
+    note(hipStreamWaitEvent(stream, ev[n], 0));
+    // a recorded event may be destroyed before it completes; its resources are
+    // released once it has
+    for (int c = 0; c <= n; ++c) (void)hipEventDestroy(ev[c]);
+  }
+  return hip_status(err, "dsa_index_attn_fwd launch");
 }
 
 DSA_EXPORT size_t dsa_sparse_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t heads,

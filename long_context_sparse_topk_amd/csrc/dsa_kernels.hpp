@@ -65,10 +65,13 @@ struct IndexArgs {
   const uint16_t* k_idx;
   const uint16_t* w_idx;
   const int32_t* q_pos;
+  int64_t q_base;          // position of row 0 when q_pos is NULL
   int64_t Sq, Sk;
   int heads, topk, q_chunk;
   int32_t* idx_out;
   void* ws;
+  int max_per_cu;          // > 0: at most this many resident workgroups per CU
+  bool pooled;             // the workspace already holds the pooled keys of k_idx
 };
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
@@ -83,6 +86,7 @@ struct AttnArgs {
   const float* lse_in;    // bwd only
   const int32_t* idx;
   const int32_t* q_pos;
+  int64_t q_base;         // fwd: position of row 0 when q_pos is NULL
   int64_t Sq, Sk;
   int heads, topk;
   float scale;

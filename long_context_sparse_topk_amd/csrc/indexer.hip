@@ -230,6 +230,7 @@ struct KernelArgs {
   const uint16_t* w_idx;
   const uint16_t* kpool;
   const int32_t* q_pos;
+  int64_t q_base;          // position of row 0 when q_pos is NULL
   int64_t Sq, Sk;
   int n_pools;
   int heads, topk, cap;
@@ -362,9 +363,9 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       {
         const int64_t qr = row_of(q0 + 16 * wave + 4 * rb + g);
         const bool ok = qr >= 0;
-        int64_t pos = qr;
-        if (ok && a.q_pos) {
-          pos = a.q_pos[qr];
+        int64_t pos = 0;
+        if (ok) {
+          pos = a.q_pos ? (int64_t)a.q_pos[qr] : a.q_base + qr;
           pos = pos < 0 ? 0 : (pos >= a.Sk ? a.Sk - 1 : pos);
         }
         nc[rb] = ok ? (int)((pos + 1) >> 2) : 0;
@@ -761,24 +762,30 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
   }
 }
 
-// Workgroups the device keeps resident at once (cached per device): the
-// persistent grid is never larger, so no slot waits for another to finish.
-int resident_index_blocks() {
+// Workgroups the device keeps resident at once, and its CU count (cached per
+// device): the persistent grid is never larger, so no slot waits for another
+// to finish.
+struct Residency {
+  int cus, per_cu;
+};
+
+Residency index_residency() {
   static std::mutex mu;
-  static int cache[64] = {0};
+  static Residency cache[64] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kIndexMaxSlots;
+  const Residency fallback{kIndexMaxSlots / 2, 2};
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fallback;
   std::lock_guard<std::mutex> lock(mu);
-  if (cache[dev] == 0) {
+  if (cache[dev].cus == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, indexer_topk_kernel<true>, kThreads, 0) !=
             hipSuccess ||
         cus * per <= 0) {
       (void)hipGetLastError();
-      return kIndexMaxSlots;
+      return fallback;
     }
-    cache[dev] = cus * per;
+    cache[dev] = Residency{cus, per};
   }
   return cache[dev];
 }
@@ -794,15 +801,17 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   const int64_t n_pools = ia.Sk / 4;
   const int64_t n_padded = index_padded_pools(ia.Sk);
   {
-    const int64_t threads = n_padded * 8;
+    // with the pooled keys already in the workspace only the counters are cleared
+    const int64_t threads = ia.pooled ? 1 : n_padded * 8;
     pool_keys_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(
-        ia.k_idx, kpool, n_pools, n_padded, fb_count);
+        ia.k_idx, kpool, n_pools, ia.pooled ? 0 : n_padded, fb_count);
   }
   KernelArgs a;
   a.q_idx = ia.q_idx;
   a.w_idx = ia.w_idx;
   a.kpool = kpool;
   a.q_pos = ia.q_pos;
+  a.q_base = ia.q_base;
   a.Sq = ia.Sq;
   a.Sk = ia.Sk;
   a.n_pools = (int)n_pools;
@@ -816,7 +825,9 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   a.cand = reinterpret_cast<u32x2_t*>(ws + L.cand_off);
   a.idx_out = ia.idx_out;
   int64_t slots = index_slots(ia.Sq);  // the workspace holds candidate lists for this many
-  const int64_t resident = resident_index_blocks();
+  const Residency res = index_residency();
+  const int per_cu = ia.max_per_cu > 0 && ia.max_per_cu < res.per_cu ? ia.max_per_cu : res.per_cu;
+  const int64_t resident = (int64_t)res.cus * per_cu;
   if (resident < slots) slots = resident;
   a.tile_next = fb_count + 1;
   indexer_topk_kernel<true><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);

@@ -135,3 +135,44 @@ def test_python_binding_checks_dtypes():
     q = torch.zeros(4, 4, 64, dtype=torch.float32)
     with pytest.raises(TypeError):
         D.index_topk(q, q[:, 0], q[:, :, 0], topk=4)
+
+
+def _pipe(**kw):
+    a = dict(q_idx=P, k_idx=P, w_idx=P, q=P, k=P, v=P, q_pos=None, Sq=64, Sk=64, HI=4, DI=64, H=4,
+             D=128, pool=4, topk=8, q_chunk=256, scale=0.1, idx=P, out=P, lse=P, ws=P,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return D.lib().dsa_index_attn_fwd(a["q_idx"], a["k_idx"], a["w_idx"], a["q"], a["k"], a["v"],
+                                      a["q_pos"], a["Sq"], a["Sk"], a["HI"], a["DI"], a["H"], a["D"],
+                                      a["pool"], a["topk"], a["q_chunk"], a["scale"], a["idx"],
+                                      a["out"], a["lse"], a["ws"], a["ws_bytes"], None, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q_idx=None), 1, "q_idx is NULL"),
+    (dict(q=None), 1, "q is NULL"),
+    (dict(v=P + 4), 1, "v is not 16-byte aligned"),
+    (dict(idx=None), 1, "idx_out is NULL"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(ws=None), 1, "ws is NULL"),
+    (dict(Sq=65, Sk=64), 1, "Sq=65 > Sk=64"),
+    (dict(DI=32), 2, "idx_dim=32"),
+    (dict(HI=5), 2, "idx_heads=5"),
+    (dict(D=64), 2, "head_dim=64"),
+    (dict(H=17), 2, "heads=17"),
+    (dict(topk=4096), 2, "topk=4096"),
+    (dict(q_chunk=0), 1, "q_chunk=0"),
+    (dict(scale=-1.0), 1, "scale"),
+    (dict(ws_bytes=100), 3, "ws_bytes=100"),
+])
+def test_pipelined_validation(kw, status, msg):
+    # validation of both stages runs on the host before any HIP call
+    assert _pipe(**kw) == status
+    assert msg in D.lib().dsa_last_error().decode()
+
+
+def test_pipelined_workspace_is_the_indexers():
+    L = D.lib()
+    for Sq, Sk, k in ((4096, 4096, 128), (1 << 20, 1 << 20, 512), (65536, 262144, 128)):
+        assert L.dsa_index_attn_fwd_ws_bytes(Sq, Sk, 4, 64, 4, k, 256) == \
+            L.dsa_index_topk_ws_bytes(Sq, Sk, 4, 64, 4, k, 256)

@@ -299,10 +299,10 @@ def test_full_size_pipeline_sampled(name):
     qp = d["q_pos"]
     dev = {k: dev_bf16(d[k]) for k in ("q_idx", "k_idx", "w_idx", "q", "k", "v")}
     tq = None if qp is None else dev_i32(qp)
-    note(f"full {name}: GPU index + fwd{' + bwd' if wl.backward else ''}")
-    idx = D.index_topk(dev["q_idx"], dev["k_idx"], dev["w_idx"], topk=wl.topk, q_chunk=wl.q_chunk,
-                       q_pos=tq)
-    out, lse = D.sparse_attn_fwd(dev["q"], dev["k"], dev["v"], idx, q_pos=tq, scale=SCALE)
+    note(f"full {name}: GPU pipelined index + fwd{' + bwd' if wl.backward else ''}")
+    # the launch configuration the benchmark times: indexer and forward pipelined over query chunks
+    idx, out, lse = D.index_attn_fwd(dev["q_idx"], dev["k_idx"], dev["w_idx"], dev["q"], dev["k"],
+                                     dev["v"], topk=wl.topk, q_chunk=wl.q_chunk, q_pos=tq, scale=SCALE)
     if wl.backward:
         tdo = dev_bf16(d["dout"])
         dq, dk, dv = D.sparse_attn_bwd(dev["q"], dev["k"], dev["v"], out, tdo, lse, idx, q_pos=tq,
@@ -403,3 +403,47 @@ def test_full_size_backward_sampled_keys(name):
     assert_close(f"{name} dq", host_f64(dq[sel]), dq_ref)
     assert_close(f"{name} dk", host_f64(dk[ks]), dk_ref)
     assert_close(f"{name} dv", host_f64(dv[ks]), dv_ref)
+
+
+# ---------------------------------------------------------------------------
+# pipelined indexer + forward: equal, bit for bit, to the two separate calls
+
+
+@pytest.mark.parametrize("Sq,Sk,H,topk,zigzag,same_stream", [
+    (300_001, 300_001, 3, 32, False, False),     # 2 chunks, ragged tail tile
+    (262_144, 1 << 20, 2, 16, True, False),      # zig-zag share: q_pos given, 2 chunks
+    (1031, 1031, 5, 16, False, False),           # one chunk
+    (300_001, 300_001, 3, 32, False, True),      # aux stream == stream: sequential
+])
+def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream):
+    rng = np.random.default_rng([Sq, H, topk])
+    qi, ki, wi = _int_inputs(Sq, Sk, seed=Sq + topk)
+    q = _bits(rng.standard_normal((Sq, H, 128)).astype(np.float32))
+    k = _bits(rng.standard_normal((Sk, 128)).astype(np.float32))
+    v = _bits(rng.standard_normal((Sk, 128)).astype(np.float32))
+    pos = syn.zigzag_positions(Sk, 2, 1)[:Sq] if zigzag else None
+    tq = None if pos is None else dev_i32(pos)
+    dqi, dki, dwi, dq, dk, dv = (dev_bf16(x) for x in (qi, ki, wi, q, k, v))
+    note(f"pipelined Sq={Sq} Sk={Sk} H={H} topk={topk} zigzag={zigzag} same_stream={same_stream}")
+    aux = torch.cuda.current_stream() if same_stream else None
+    idx_p, out_p, lse_p = D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, q_pos=tq,
+                                           scale=SCALE, aux_stream=aux)
+    idx_s = D.index_topk(dqi, dki, dwi, topk=topk, q_pos=tq)
+    out_s, lse_s = D.sparse_attn_fwd(dq, dk, dv, idx_s, q_pos=tq, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx_s), "pipelined idx differs from dsa_index_topk"
+    assert torch.equal(out_p, out_s), "pipelined out differs from dsa_sparse_attn_fwd"
+    assert torch.equal(lse_p, lse_s), "pipelined lse differs from dsa_sparse_attn_fwd"
+    # and the oracle on sampled rows, chunk boundaries included
+    bounds = [int(round(Sq * np.sqrt(c / 2) / 64)) * 64 for c in (1,)]
+    rows = np.unique(np.concatenate([sample_rows(Sq, topk, pos, n_random=24),
+                                     [b + d for b in bounds for d in (-1, 0, 1) if 0 <= b + d < Sq]]))
+    ref_idx = O.index_topk(qi, ki, wi, pos, topk, rows=rows)
+    assert_idx_equal("pipelined idx", idx_p[torch.from_numpy(rows).cuda()].cpu().numpy(), ref_idx, rows)
+    full_idx = np.zeros((Sq, topk), np.int32)
+    full_idx[rows] = ref_idx
+    o_ref, lse_ref = O.sparse_attn_fwd(q, k, v, full_idx, pos, SCALE, rows=rows)
+    sel = torch.from_numpy(rows).cuda()
+    assert_close("pipelined O", host_f64(out_p[sel]), o_ref)
+    assert_close("pipelined lse", host_f64(lse_p[sel]), lse_ref, max_abs=LSE_ABS, mean_abs=LSE_ABS,
+                 rel=1e-4)
