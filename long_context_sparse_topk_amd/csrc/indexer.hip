@@ -47,6 +47,7 @@ constexpr int kBufferWord3 = 0x00020000;  // raw buffer: 32-bit data format, no 
 constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
 constexpr int kWaitVmcnt2 = 0x0F72;        // s_waitcnt vmcnt(2) expcnt(7) lgkmcnt(15)
 constexpr int kRing = 3;                   // LDS key-tile buffers
+constexpr int kExactSharedSlots = 64;      // exact-pass grid when the CUs are shared
 
 // ---------------------------------------------------------------------------
 
@@ -831,9 +832,12 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   if (resident < slots) slots = resident;
   a.tile_next = fb_count + 1;
   indexer_topk_kernel<true><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
-  // queries whose threshold estimate was too high twice, scored exactly
+  // queries whose threshold estimate was too high twice, scored exactly.  They are
+  // rare (none to a few per 2^16 rows on the workloads); when other kernels share
+  // the CUs, a small grid finds free slots sooner than one workgroup per CU would.
   a.tile_next = fb_count + 2;
-  indexer_topk_kernel<false><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
+  const int64_t exact_slots = ia.max_per_cu > 0 && slots > kExactSharedSlots ? kExactSharedSlots : slots;
+  indexer_topk_kernel<false><<<dim3((unsigned)exact_slots), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -447,3 +447,26 @@ def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream):
     assert_close("pipelined O", host_f64(out_p[sel]), o_ref)
     assert_close("pipelined lse", host_f64(lse_p[sel]), lse_ref, max_abs=LSE_ABS, mean_abs=LSE_ABS,
                  rel=1e-4)
+
+
+def test_pipelined_exact_fallback():
+    # the threshold trap at two chunks: nearly every row fails both sampled thresholds, so the
+    # exact pass (a small grid while the forward shares the CUs) scores them
+    S, topk, H = 262_144 + 100, 64, 1
+    k_idx = _threshold_trap_keys(S, 10)
+    qi = _bits(np.ones((S, 4, 64), np.float32))
+    wi = _bits(np.ones((S, 4), np.float32))
+    rng = np.random.default_rng(5)
+    q = _bits(rng.standard_normal((S, H, 128)).astype(np.float32))
+    k = _bits(rng.standard_normal((S, 128)).astype(np.float32))
+    v = _bits(rng.standard_normal((S, 128)).astype(np.float32))
+    note("pipelined threshold trap, 2 chunks")
+    dqi, dki, dwi, dq, dk, dv = (dev_bf16(x) for x in (qi, k_idx, wi, q, k, v))
+    idx_p, out_p, lse_p = D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, scale=SCALE)
+    idx_s = D.index_topk(dqi, dki, dwi, topk=topk)
+    out_s, lse_s = D.sparse_attn_fwd(dq, dk, dv, idx_s, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx_s) and torch.equal(out_p, out_s) and torch.equal(lse_p, lse_s)
+    rows = sample_rows(S, topk, None, n_random=16)
+    ref = O.index_topk(qi, k_idx, wi, None, topk, rows=rows)
+    assert_idx_equal("pipelined trap idx", idx_p[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, rows)
