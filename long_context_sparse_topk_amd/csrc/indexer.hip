@@ -645,8 +645,13 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
             // all 4 stages of a wave are flushed together, when one of them
             // could not take another tile's worth (4 x 64 entries), and every
             // kFlushPeriod tiles (the same tiles in every wave).
-            // scalar-only tests: full = some count > kStage - 256 (the sign
-            // bit of count - (kStage - 255) is clear), fl = counts > 0
+            // No stage can be within one tile of its end while the four
+            // counts together are at most kStage - 256: one scalar test on
+            // most tiles.  Otherwise, scalar-only tests: full = some count >
+            // kStage - 256 (the sign bit of count - (kStage - 255) is clear),
+            // fl = counts > 0.
+            const bool period = i > 0 && (i % kFlushPeriod) == 0;
+            if (!period && nst[0] + nst[1] + nst[2] + nst[3] <= kStage - 4 * kWave) return;
             int neg = -1;
             uint32_t fl = 0;
 #pragma unroll
@@ -655,7 +660,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
               fl |= ((uint32_t)(-nst[rb]) >> 31) << rb;
             }
             const bool full = neg >= 0;
-            if (!(full || (i > 0 && (i % kFlushPeriod) == 0)) || fl == 0) return;
+            if (!(full || period) || fl == 0) return;
             flush(fl);
             bool fenced = false;
             for (uint32_t m = fl; m != 0; m &= m - 1) {
