@@ -470,3 +470,20 @@ def test_pipelined_exact_fallback():
     rows = sample_rows(S, topk, None, n_random=16)
     ref = O.index_topk(qi, k_idx, wi, None, topk, rows=rows)
     assert_idx_equal("pipelined trap idx", idx_p[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, rows)
+
+
+def test_s4k_workload_every_row():
+    # the S = 4096 workload (H = 4, top-128, its own seeded inputs) through the benchmark's entry
+    # point, compared element by element on every row: idx exactly, O and LSE to tolerance
+    wl = syn.WORKLOADS["s4k"]
+    d = syn.make_inputs(wl, parts=("index", "attn"))
+    note("s4k workload, every row")
+    t = {n: dev_bf16(d[n]) for n in ("q_idx", "k_idx", "w_idx", "q", "k", "v")}
+    idx, out, lse = D.index_attn_fwd(t["q_idx"], t["k_idx"], t["w_idx"], t["q"], t["k"], t["v"],
+                                     topk=wl.topk, q_chunk=wl.q_chunk, scale=SCALE)
+    torch.cuda.synchronize()
+    ref_idx = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], None, wl.topk)
+    assert_idx_equal("s4k idx", idx.cpu().numpy(), ref_idx)
+    o_ref, lse_ref = O.sparse_attn_fwd(d["q"], d["k"], d["v"], ref_idx, None, SCALE)
+    assert_close("s4k O", host_f64(out), o_ref)
+    assert_close("s4k lse", host_f64(lse), lse_ref, max_abs=LSE_ABS, mean_abs=LSE_ABS, rel=1e-4)
