@@ -107,6 +107,15 @@ def _want(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device: tor
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t, name: str, dtype: torch.dtype, shape: tuple, device: torch.device):
+    """A caller-provided buffer the kernels write: dtype, device, contiguity and exact shape,
+    so that no write can leave it."""
+    _want(t, name, dtype, len(shape), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def _positions(q_pos, Sq, device):
     if q_pos is None:
         return None
@@ -146,10 +155,12 @@ def index_topk(q_idx, k_idx, w_idx, *, topk: int, q_chunk: int = 256, q_pos=None
     if out is None:
         out = torch.empty((Sq, topk), dtype=torch.int32, device=dev)
     else:
-        _want(out, "out", torch.int32, 2, dev)
+        _out(out, "out", torch.int32, (Sq, topk), dev)
     need = int(L.dsa_index_topk_ws_bytes(Sq, Sk, HI, DI, POOL, topk, q_chunk))
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    else:
+        _want(ws, "ws", torch.uint8, 1, dev)
     st = L.dsa_index_topk(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q_pos), Sq, Sk, HI, DI, POOL,
                           topk, q_chunk, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream(dev))
@@ -171,10 +182,9 @@ def sparse_attn_fwd(q, k, v, idx, *, q_pos=None, scale: float | None = None, out
         raise ValueError("attention shapes disagree")
     q_pos = _positions(q_pos, Sq, dev)
     scale = default_scale(D) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((Sq, H), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q) if out is None else _out(out, "out", torch.bfloat16, (Sq, H, D), dev)
+    lse = (torch.empty((Sq, H), dtype=torch.float32, device=dev) if lse is None
+           else _out(lse, "lse", torch.float32, (Sq, H), dev))
     st = L.dsa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(q_pos), Sq, Sk, H, D, POOL,
                                idx.shape[1], scale, _ptr(out), _ptr(lse), _stream(dev))
     _check("dsa_sparse_attn_fwd", st)
@@ -217,13 +227,16 @@ def index_attn_fwd(q_idx, k_idx, w_idx, q, k, v, *, topk: int, q_chunk: int = 25
         raise ValueError("attention shapes disagree")
     q_pos = _positions(q_pos, Sq, dev)
     scale = default_scale(D) if scale is None else float(scale)
-    idx = torch.empty((Sq, topk), dtype=torch.int32, device=dev) if idx is None else idx
-    _want(idx, "idx", torch.int32, 2, dev)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((Sq, H), dtype=torch.float32, device=dev) if lse is None else lse
+    idx = (torch.empty((Sq, topk), dtype=torch.int32, device=dev) if idx is None
+           else _out(idx, "idx", torch.int32, (Sq, topk), dev))
+    out = torch.empty_like(q) if out is None else _out(out, "out", torch.bfloat16, (Sq, H, D), dev)
+    lse = (torch.empty((Sq, H), dtype=torch.float32, device=dev) if lse is None
+           else _out(lse, "lse", torch.float32, (Sq, H), dev))
     need = int(L.dsa_index_attn_fwd_ws_bytes(Sq, Sk, HI, DI, POOL, topk, q_chunk))
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    else:
+        _want(ws, "ws", torch.uint8, 1, dev)
     aux = _aux_stream(dev) if aux_stream is None else aux_stream
     st = L.dsa_index_attn_fwd(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(v),
                               _ptr(q_pos), Sq, Sk, HI, DI, H, D, POOL, topk, q_chunk, scale,
@@ -247,12 +260,17 @@ def sparse_attn_bwd(q, k, v, out, dout, lse, idx, *, q_pos=None, scale: float | 
     Sk = k.shape[0]
     q_pos = _positions(q_pos, Sq, dev)
     scale = default_scale(D) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    if tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != (Sq, H, D) or \
+            tuple(dout.shape) != (Sq, H, D) or tuple(lse.shape) != (Sq, H) or idx.shape[0] != Sq:
+        raise ValueError("attention shapes disagree")
+    dq = torch.empty_like(q) if dq is None else _out(dq, "dq", torch.bfloat16, (Sq, H, D), dev)
+    dk = torch.empty_like(k) if dk is None else _out(dk, "dk", torch.bfloat16, (Sk, D), dev)
+    dv = torch.empty_like(v) if dv is None else _out(dv, "dv", torch.bfloat16, (Sk, D), dev)
     need = int(L.dsa_sparse_attn_bwd_ws_bytes(Sq, Sk, H, D, idx.shape[1]))
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    else:
+        _want(ws, "ws", torch.uint8, 1, dev)
     st = L.dsa_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(idx),
                                _ptr(q_pos), Sq, Sk, H, D, POOL, idx.shape[1], scale, _ptr(dq),
                                _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),

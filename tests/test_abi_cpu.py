@@ -176,3 +176,27 @@ def test_pipelined_workspace_is_the_indexers():
     for Sq, Sk, k in ((4096, 4096, 128), (1 << 20, 1 << 20, 512), (65536, 262144, 128)):
         assert L.dsa_index_attn_fwd_ws_bytes(Sq, Sk, 4, 64, 4, k, 256) == \
             L.dsa_index_topk_ws_bytes(Sq, Sk, 4, 64, 4, k, 256)
+
+
+def test_python_binding_checks_output_shapes():
+    # caller-provided outputs must match exactly, so no kernel write can leave them
+    # (the checks raise before any library call)
+    import torch
+    bf = torch.bfloat16
+    qi, ki, wi = torch.zeros(64, 4, 64, dtype=bf), torch.zeros(64, 64, dtype=bf), torch.zeros(64, 4, dtype=bf)
+    q, k, v = torch.zeros(64, 2, 128, dtype=bf), torch.zeros(64, 128, dtype=bf), torch.zeros(64, 128, dtype=bf)
+    idx = torch.zeros(64, 8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        D.index_topk(qi, ki, wi, topk=8, out=torch.zeros(63, 8, dtype=torch.int32))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        D.sparse_attn_fwd(q, k, v, idx, lse=torch.zeros(64, 3, dtype=torch.float32))
+    with pytest.raises(ValueError, match="out must have shape"):
+        D.sparse_attn_fwd(q, k, v, idx, out=torch.zeros(64, 2, 64, dtype=bf))
+    with pytest.raises(ValueError, match="idx must have shape"):
+        D.index_attn_fwd(qi, ki, wi, q, k, v, topk=8, idx=torch.zeros(64, 4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="dk must have shape"):
+        D.sparse_attn_bwd(q, k, v, q, q, torch.zeros(64, 2), idx, dk=torch.zeros(32, 128, dtype=bf))
+    with pytest.raises(ValueError, match="attention shapes disagree"):
+        D.sparse_attn_bwd(q, k, v, q, q, torch.zeros(64, 3), idx)
+    with pytest.raises(TypeError, match="ws must be"):
+        D.index_topk(qi, ki, wi, topk=8, ws=torch.zeros(1 << 20, dtype=torch.float32))
