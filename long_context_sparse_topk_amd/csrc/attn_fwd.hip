@@ -58,9 +58,10 @@ __device__ __forceinline__ int2 slot_info(const int32_t* irow, int ps, int np, i
   return make_int2(base, nv);
 }
 
+template <bool kPrefetch>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   __shared__ __align__(16) uint16_t lds_v[kRows][32 * kVStride];
-  __shared__ int2 lds_info[kRows][8];
+  __shared__ int2 lds_info[kRows][kPrefetch ? 2 : 1][8];  // slot info, double buffered when prefetching
 
   const int lane = lane_id();
   const int wave = uniform(threadIdx.x >> 6);
@@ -100,18 +101,49 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m2 = NEG_INF, lsum = 0.f;
   uint16_t* vt = lds_v[wave];
-  int2* info = lds_info[wave];
 
-  for (int t = 0; t < ntile; ++t) {
-    if (lane < 8) info[lane] = slot_info(irow, 8 * t + lane, np, nc, part, pos);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-
-    // K rows -> A operands, V rows -> registers: all 16 loads of the tile are
-    // issued before any is waited on, so the tile costs one memory round trip
+  // Two schedules.  kPrefetch (the kernel has the GPU to itself): the K/V
+  // rows of the next tile are in flight while a tile is computed, with two
+  // register buffers and the loop unrolled by two; loads past the last tile
+  // read the query's own key row (no valid key there), so every step issues
+  // its 16 loads.  Otherwise (the kernel shares the CUs with the indexer): one
+  // tile's 16 loads at a time, which keeps the wave at 176 registers so that
+  // it fits beside an indexer wave on a SIMD and leaves that wave the issue
+  // slots.  Slot info is double buffered in LDS.
+  struct Buf {
     bf16x8_t KA[2][4];
     u32x4_t VR[2][4];
-    uint16_t* vdst[2];
+  };
+  // slot ids of tile t: lane j (mod 8) reads id 8t + j, clamped into the row
+  // so the load is unconditional (ids at or past np are not used)
+  auto load_ids = [&](int t) -> int {
+    const int ps = 8 * t + (lane & 7);
+    const int cps = ps < np ? ps : (np > 0 ? np - 1 : 0);
+    return irow[cps];
+  };
+  // slot info of tile t from its id (lanes < 8), as slot_info computes it
+  auto set_info = [&](int t, int id) {
+    int2* info = lds_info[wave][kPrefetch ? (t & 1) : 0];
+    if (lane < 8) {
+      const int ps = 8 * t + lane;
+      int base = pos, nv = 0;
+      if (ps < np) {
+        if (id >= 0 && id < nc) {
+          base = 4 * id;
+          nv = 4;
+        }
+      } else if (ps == np && part > 0) {
+        base = 4 * nc;
+        nv = part;
+      }
+      info[lane] = make_int2(base, nv);
+    }
+  };
+  // the 16 K/V row loads of tile t (after its slot info is in LDS)
+  auto load_kv = [&](int t, Buf& B) {
+    const int2* info = lds_info[wave][kPrefetch ? (t & 1) : 0];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int2 in = info[4 * kb + (c16 >> 2)];
@@ -119,25 +151,27 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
       const int64_t key = off < in.y ? in.x + off : pos;
       const uint16_t* ks_src = a.k + key * kD + 8 * g;
       const uint16_t* vs_src = a.v + key * kD + 8 * g;
-      vdst[kb] = vt + (16 * kb + c16) * kVStride + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        KA[kb][ks] = load_bf16x8(ks_src + 32 * ks);
-        VR[kb][ks] = *reinterpret_cast<const u32x4_t*>(vs_src + 32 * ks);
+        B.KA[kb][ks] = load_bf16x8(ks_src + 32 * ks);
+        B.VR[kb][ks] = *reinterpret_cast<const u32x4_t*>(vs_src + 32 * ks);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute = [&](int t, const Buf& B) {
+    const int2* info = lds_info[wave][kPrefetch ? (t & 1) : 0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      uint16_t* vdst = vt + (16 * kb + c16) * kVStride + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4_t*>(vdst[kb] + 32 * ks) = VR[kb][ks];
-
+      for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4_t*>(vdst + 32 * ks) = B.VR[kb][ks];
+    }
     f32x4_t S[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       S[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) S[kb] = mfma32(KA[kb][ks], QB[ks], S[kb]);
+      for (int ks = 0; ks < 4; ++ks) S[kb] = mfma32(B.KA[kb][ks], QB[ks], S[kb]);
     }
 
     // lane holds keys 16*kb + 4*g + rr (pool slot 4*kb + g, offset rr) of head c16
@@ -192,6 +226,47 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
+  };
+
+  if constexpr (kPrefetch) {
+    // ids are loaded one step before the K/V loads that use them, so no wait
+    // for them drains the tile in flight
+    Buf B0, B1;
+    int id = load_ids(0);
+    if (ntile > 0) {
+      const int id0 = id;
+      id = load_ids(1);
+      set_info(0, id0);
+      load_kv(0, B0);
+    }
+    for (int t = 0; t < ntile; t += 2) {
+      {
+        const int idt = id;
+        id = load_ids(t + 2);
+        set_info(t + 1, idt);
+        load_kv(t + 1, B1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t, B0);
+      if (t + 1 >= ntile) break;
+      {
+        const int idt = id;
+        id = load_ids(t + 3);
+        set_info(t + 2, idt);
+        load_kv(t + 2, B0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t + 1, B1);
+    }
+  } else {
+    // one tile at a time: its 16 loads are issued together, then waited on
+    Buf B;
+    for (int t = 0; t < ntile; ++t) {
+      if (lane < 8) lds_info[wave][kPrefetch ? (t & 1) : 0][lane] = slot_info(irow, 8 * t + lane, np, nc, part, pos);
+      load_kv(t, B);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t, B);
+    }
   }
 
   float lt = lsum + __shfl_xor(lsum, 16, kWave);
@@ -228,7 +303,10 @@ hipError_t launch_attn_fwd(const AttnArgs& x, hipStream_t s) {
   a.out = x.out;
   a.lse = x.lse_out;
   const int64_t blocks = (x.Sq + kRows - 1) / kRows;
-  attn_fwd_kernel<<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+  if (x.fwd_shared)
+    attn_fwd_kernel<false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+  else
+    attn_fwd_kernel<true><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
   return hipGetLastError();
 }
 

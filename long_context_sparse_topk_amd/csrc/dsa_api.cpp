@@ -294,6 +294,7 @@ DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const vo
     fa.scale = scale;
     fa.out = oo + r0 * heads * head_dim;
     fa.lse_out = lse + r0 * heads;
+    fa.fwd_shared = n > 1 && c + 1 < n;   // the last chunk's forward runs after the indexer
     note(dsa::launch_attn_fwd(fa, fs));
   }
   if (n > 1) {

@@ -95,6 +95,7 @@ struct AttnArgs {
   uint16_t* dk;           // bwd only
   uint16_t* dv;           // bwd only
   void* ws;               // bwd only
+  bool fwd_shared;        // fwd: the launch shares the CUs with the indexer (lean schedule)
 };
 
 // Backward workspace: per (row, head) a 16-byte record (LSE in log2 units,
