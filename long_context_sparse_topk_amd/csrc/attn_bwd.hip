@@ -57,22 +57,6 @@ struct BwdArgs {
   float* stats;            // per (row, head): lse * log2(e), Delta, position (bits), 0
 };
 
-__device__ __forceinline__ int2 slot_info(const int32_t* irow, int ps, int np, int nc, int part,
-                                          int pos) {
-  int base = pos, nv = 0;
-  if (ps < np) {
-    const int p = irow[ps];
-    if (p >= 0 && p < nc) {
-      base = 4 * p;
-      nv = 4;
-    }
-  } else if (ps == np && part > 0) {
-    base = 4 * nc;
-    nv = part;
-  }
-  return make_int2(base, nv);
-}
-
 __device__ __forceinline__ int clamp_pos(const int32_t* q_pos, int64_t r, int64_t Sk) {
   int64_t pos = r;
   if (q_pos) {
@@ -82,9 +66,9 @@ __device__ __forceinline__ int clamp_pos(const int32_t* q_pos, int64_t r, int64_
   return (int)pos;
 }
 
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __align__(16) uint16_t lds_k[kRows][32 * kKStride];
-  __shared__ int2 lds_info[kRows][8];
+  __shared__ int2 lds_info[kRows][2][8];
 
   const int lane = lane_id();
   const int wave = uniform(threadIdx.x >> 6);
@@ -142,14 +126,42 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < 8; ++db) dqa[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint16_t* kt = lds_k[wave];
-  int2* info = lds_info[wave];
 
-  for (int t = 0; t < ntile; ++t) {
-    if (lane < 8) info[lane] = slot_info(irow, 8 * t + lane, np, nc, part, pos);
+  // The K/V rows of the next tile are in flight while a tile is computed (two
+  // register buffers, the loop unrolled by two); its slot ids are loaded one
+  // step earlier still, so no wait on them drains the tile in flight.  Loads
+  // past the last tile read the query's own key row.  Slot info is double
+  // buffered in LDS.
+  struct Buf {
+    bf16x8_t KA[2][4], VA[2][4];
+  };
+  // slot ids of tile t: lane j (mod 8) reads id 8t + j, clamped into the row
+  auto load_ids = [&](int t) -> int {
+    const int ps = 8 * t + (lane & 7);
+    const int cps = ps < np ? ps : (np > 0 ? np - 1 : 0);
+    return irow[cps];
+  };
+  auto set_info = [&](int t, int id) {
+    int2* info = lds_info[wave][t & 1];
+    if (lane < 8) {
+      const int ps = 8 * t + lane;
+      int base = pos, nv = 0;
+      if (ps < np) {
+        if (id >= 0 && id < nc) {
+          base = 4 * id;
+          nv = 4;
+        }
+      } else if (ps == np && part > 0) {
+        base = 4 * nc;
+        nv = part;
+      }
+      info[lane] = make_int2(base, nv);
+    }
+  };
+  auto load_kv = [&](int t, Buf& B) {
+    const int2* info = lds_info[wave][t & 1];
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
-
-    bf16x8_t KA[2][4], VA[2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int2 in = info[4 * kb + (c16 >> 2)];
@@ -157,24 +169,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
       const int64_t key = off < in.y ? in.x + off : pos;
       const uint16_t* ksrc = a.k + key * kD + 8 * g;
       const uint16_t* vsrc = a.v + key * kD + 8 * g;
-      uint16_t* kdst = kt + (16 * kb + c16) * kKStride + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(ksrc + 32 * ks);
-        KA[kb][ks] = as_bf16x8(kv);
-        *reinterpret_cast<u32x4_t*>(kdst + 32 * ks) = kv;
-        VA[kb][ks] = load_bf16x8(vsrc + 32 * ks);
+        B.KA[kb][ks] = load_bf16x8(ksrc + 32 * ks);
+        B.VA[kb][ks] = load_bf16x8(vsrc + 32 * ks);
       }
     }
-
+  };
+  auto compute = [&](int t, const Buf& B) {
+    const int2* info = lds_info[wave][t & 1];
+    // K rows also go to LDS, to be read transposed for dQ
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint16_t* kdst = kt + (16 * kb + c16) * kKStride + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<u32x4_t*>(kdst + 32 * ks) = __builtin_bit_cast(u32x4_t, B.KA[kb][ks]);
+    }
     float ds[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        s = mfma32(KA[kb][ks], QB[ks], s);
-        dp = mfma32(VA[kb][ks], DB[ks], dp);
+        s = mfma32(B.KA[kb][ks], QB[ks], s);
+        dp = mfma32(B.VA[kb][ks], DB[ks], dp);
       }
       const int nv = info[4 * kb + g].y;
 #pragma unroll
@@ -205,6 +224,34 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
+  };
+
+  Buf B0, B1;
+  int id = load_ids(0);
+  if (ntile > 0) {
+    const int id0 = id;
+    id = load_ids(1);
+    set_info(0, id0);
+    load_kv(0, B0);
+  }
+  for (int t = 0; t < ntile; t += 2) {
+    {
+      const int idt = id;
+      id = load_ids(t + 2);
+      set_info(t + 1, idt);
+      load_kv(t + 1, B1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t, B0);
+    if (t + 1 >= ntile) break;
+    {
+      const int idt = id;
+      id = load_ids(t + 3);
+      set_info(t + 2, idt);
+      load_kv(t + 2, B0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t + 1, B1);
   }
 
   if (hv) {
