@@ -487,3 +487,36 @@ def test_s4k_workload_every_row():
     o_ref, lse_ref = O.sparse_attn_fwd(d["q"], d["k"], d["v"], ref_idx, None, SCALE)
     assert_close("s4k O", host_f64(out), o_ref)
     assert_close("s4k lse", host_f64(lse), lse_ref, max_abs=LSE_ABS, mean_abs=LSE_ABS, rel=1e-4)
+
+
+@pytest.mark.parametrize("Sq,Sk,H,topk,permute", [
+    (262_144 + 64, 600_000, 2, 64, True),     # 2 chunks, positions in no order, caller's stream
+    (262_144, 262_144, 16, 2048, False),      # 2 chunks at the largest k (up to 8195 keys a row)
+])
+def test_pipelined_positions_and_largest_k(Sq, Sk, H, topk, permute):
+    rng = np.random.default_rng([Sq, topk, 3])
+    qi, ki, wi = _int_inputs(Sq, Sk, seed=topk + 5)
+    q = _bits(rng.standard_normal((Sq, H, 128)).astype(np.float32))
+    k = _bits(rng.standard_normal((Sk, 128)).astype(np.float32))
+    v = _bits(rng.standard_normal((Sk, 128)).astype(np.float32))
+    pos = rng.choice(Sk, size=Sq, replace=False).astype(np.int32) if permute else None
+    tq = None if pos is None else dev_i32(pos)
+    dqi, dki, dwi, dq, dk, dv = (dev_bf16(x) for x in (qi, ki, wi, q, k, v))
+    note(f"pipelined Sq={Sq} Sk={Sk} H={H} topk={topk} permute={permute}")
+    aux = torch.cuda.Stream()   # a second stream of the caller's own
+    idx_p, out_p, lse_p = D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, q_pos=tq, scale=SCALE,
+                                           aux_stream=aux)
+    idx_s = D.index_topk(dqi, dki, dwi, topk=topk, q_pos=tq)
+    out_s, lse_s = D.sparse_attn_fwd(dq, dk, dv, idx_s, q_pos=tq, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx_s) and torch.equal(out_p, out_s) and torch.equal(lse_p, lse_s)
+    rows = sample_rows(Sq, topk, pos, n_random=16)
+    ref_idx = O.index_topk(qi, ki, wi, pos, topk, rows=rows)
+    sel = torch.from_numpy(rows).cuda()
+    assert_idx_equal("pipelined idx", idx_p[sel].cpu().numpy(), ref_idx, rows)
+    full_idx = np.zeros((Sq, topk), np.int32)
+    full_idx[rows] = ref_idx
+    o_ref, lse_ref = O.sparse_attn_fwd(q, k, v, full_idx, pos, SCALE, rows=rows)
+    assert_close("pipelined O", host_f64(out_p[sel]), o_ref)
+    assert_close("pipelined lse", host_f64(lse_p[sel]), lse_ref, max_abs=LSE_ABS, mean_abs=LSE_ABS,
+                 rel=1e-4)
