@@ -289,7 +289,10 @@ def main():
     dk = kern[dom]
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": round(dk["achieved"], 2), "peak": dk["peak"],
                 "unit": dk["unit"], "frac": round(dk["achieved"] / dk["peak"], 4),
-                "traffic": measured_traffic(dom, wl.name), "ms_per_launch": round(dk["s"] * 1e3, 3)}
+                "traffic": measured_traffic(dom, wl.name), "ms_per_launch": round(dk["s"] * 1e3, 3),
+                # inside the pipelined step the kernels share the CUs, so the launch durations come
+                # from the pass of separate calls right after the timed steps
+                "launches": "separate calls after the timed steps"}
     kernels = {n: {"ms": round(v["s"] * 1e3, 3), "achieved": round(v["achieved"], 2), "unit": v["unit"],
                    "frac": round(v["achieved"] / v["peak"], 4)} for n, v in kern.items()}
 
