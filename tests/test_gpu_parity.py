@@ -291,7 +291,7 @@ FULL = ["s32k", "s128k", "zigzag4", "s1m"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_pipeline_sampled(name):
+def test_full_size_pipeline(name):
     wl = syn.WORKLOADS[name]
     parts = ("index", "attn", "bwd") if wl.backward else ("index", "attn")
     note(f"full {name}: generating inputs")
@@ -308,8 +308,10 @@ def test_full_size_pipeline_sampled(name):
         dq, dk, dv = D.sparse_attn_bwd(dev["q"], dev["k"], dev["v"], out, tdo, lse, idx, q_pos=tq,
                                        scale=SCALE)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.sq, wl.topk, qp)
-    note(f"full {name}: oracle on {rows.shape[0]} sampled rows")
+    # every row, except at S = 1M: there the edge rows and 4096 random ones
+    full_rows = name != "s1m"
+    rows = np.arange(wl.sq) if full_rows else sample_rows(wl.sq, wl.topk, qp, n_random=4096)
+    note(f"full {name}: oracle on {rows.shape[0]} rows")
     ref_idx = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], qp, wl.topk, rows=rows)
     got_idx = idx[torch.from_numpy(rows).cuda()].cpu().numpy()
     assert_idx_equal(f"{name} idx", got_idx, ref_idx, rows)
@@ -321,9 +323,12 @@ def test_full_size_pipeline_sampled(name):
     assert_close(f"{name} O", host_f64(out[sel]), o_ref)
     assert_close(f"{name} lse", host_f64(lse[sel]), lse_ref, max_abs=LSE_ABS, mean_abs=LSE_ABS, rel=1e-4)
     if wl.backward:
-        dq_ref, _, _ = O.sparse_attn_bwd(d["q"], d["k"], d["v"], d["dout"], full_idx, qp, SCALE,
-                                         rows=rows, key_rows=np.empty(0, np.int64))
+        # every row's dq and every key's dK, dV (the oracle's selection is the whole idx here)
+        dq_ref, dk_ref, dv_ref = O.sparse_attn_bwd(d["q"], d["k"], d["v"], d["dout"], full_idx, qp,
+                                                   SCALE, rows=rows)
         assert_close(f"{name} dq", host_f64(dq[sel]), dq_ref)
+        assert_close(f"{name} dk", host_f64(dk), dk_ref)
+        assert_close(f"{name} dv", host_f64(dv), dv_ref)
         # properties that hold at any size: sum_j dV[j] = sum_{r,h} dO[r,h];
         # sum_j dK[j] = scale * sum_{r,h} (sum_j dS) q = 0 up to bf16 rounding of O
         sdv = host_f64(dv).sum(axis=0)
