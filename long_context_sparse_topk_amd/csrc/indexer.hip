@@ -395,8 +395,11 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     const int64_t wbase = ((int64_t)blockIdx.x * kQT + 16 * wave) * cap;
 
     // Pool-key tiles go straight from HBM to LDS (buffer loads with the LDS
-    // destination) through a ring of kRing buffers, two tiles ahead of the
-    // one being scored.  Lane l of a load instruction writes LDS chunk
+    // destination) through a ring of kRing buffers, issued two tiles ahead of
+    // the one being scored.  (The workgroup barrier releases LDS, and these
+    // loads write LDS, so the compiler waits for all of them before each
+    // barrier: a tile's loads have one tile's scoring time to land.)  Lane l
+    // of a load instruction writes LDS chunk
     // (base + l); its source offset is chosen so that LDS row pr, chunk ch
     // holds key chunk ch ^ (pr & 7) (the swizzle that spreads the B-operand
     // reads over the banks).  The loads are unconditional (the keys are
