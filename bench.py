@@ -243,6 +243,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="s1m", choices=sorted(syn.WORKLOADS))
     ap.add_argument("--secondary", default="s128k", help="second workload timed in the same run ('' = none)")
+    ap.add_argument("--others", default="s4k,s32k,zigzag4",
+                    help="further workloads timed in the same run, comma-separated ('' = none)")
     ap.add_argument("--cpu-rows", type=int, default=512, help="oracle sample size (rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -322,6 +324,27 @@ def main():
             secondary["bwd_ws_bytes"] = int(sl.ws_bwd.numel())
         del sl
 
+    # the remaining workloads: throughput, the indexer's fraction of the MFMA peak and the
+    # attention kernels' algorithmic bytes per second
+    others = []
+    for name in [n for n in args.others.split(",") if n and n not in (wl.name, args.secondary)]:
+        ow = syn.WORKLOADS[name]
+        ol = Layer(ow, device)
+        owall, oavg, ostep = run(ol, args.steps, args.warmup)
+        ows = work(ow)
+        rec = {"workload": ow.name, "tokens_per_s": round(ow.sq * args.steps / owall, 1),
+               "ms_per_step": round(owall / args.steps * 1e3, 3),
+               "pass": "index+fwd+bwd" if ow.backward else "index+fwd",
+               "ms": {k: round(v * 1e3, 3) for k, v in oavg.items()},
+               "index_mfma_frac": round(ows["index_flop"] / oavg["index"] / BF16_PEAK, 4),
+               # algorithmic bytes per second; K and V of these workloads (8 to 64 MiB) stay in
+               # the caches, so the rate can exceed the HBM peak
+               "fwd_gather_GBps": round(ows["fwd_bytes"] / oavg["fwd"] / 1e9, 1)}
+        if ow.backward:
+            rec["bwd_GBps"] = round(ows["bwd_bytes"] / oavg["bwd"] / 1e9, 1)
+        others.append(rec)
+        del ol
+
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle CPU baseline")
@@ -354,6 +377,7 @@ def main():
         "fwd_gather_GBps": round(w["fwd_bytes"] / avg["fwd"] / 1e9, 1),
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "others": others,
     }
     print(json.dumps(line), flush=True)
 
