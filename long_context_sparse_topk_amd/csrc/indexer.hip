@@ -8,8 +8,9 @@
 //
 // Kernels:
 //   pool_keys_kernel    kpool[p] = bf16(mean of k_idx[4p..4p+3])   (HBM-bound)
-//   indexer_topk_kernel per workgroup sub-tile of 64 queries (256 rows of
-//                       query x indexer-head), stream the causal pool range in
+//   indexer_topk_kernel per workgroup sub-tile of 64 queries, 16 a wave (256
+//                       rows of query x indexer-head; 16 queries, 4 a wave, on
+//                       a short key range), stream the causal pool range in
 //                       tiles of 64 pools staged in LDS; bf16 MFMA 16x16x32 gives
 //                       the 4 head dot products of a (query, pool) pair in one
 //                       lane (head weights folded into the query operand), so
@@ -30,6 +31,8 @@
 // pool order.
 
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "dsa_device.hpp"
@@ -39,9 +42,9 @@ namespace dsa {
 namespace {
 
 constexpr int kDI = 64;              // indexer head dim
-constexpr int kQT = kIndexQueryTile; // 64 queries per sub-tile
+constexpr int kQT = kIndexQueryTile; // queries per sub-tile of the wider variant
 constexpr int kPT = kIndexPoolTile;  // 64 pools per staged tile
-constexpr int kWaves = 4;            // 16 queries per wave
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer: 32-bit data format, no swizzle
 constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
@@ -299,10 +302,12 @@ __device__ __forceinline__ bf16x8_t fold_weight(u32x4_t q, float w) {
 // per-query lists in HBM (stable per query, so each list stays in pool
 // order).  Keeping global stores out of the scoring loop keeps the prefetch
 // wait exact (loads and stores share one completion counter).
-template <bool kTwoPhase>
+template <bool kTwoPhase, int kRB>
 __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a) {
+  constexpr int kQW = 4 * kRB;        // queries per wave (kRB row blocks of 4)
+  constexpr int kQTile = kWaves * kQW;  // queries per workgroup tile
   __shared__ __align__(16) u32x4_t lds_k[kRing][kPT * 8];   // ring of (64 pools x 128 B), swizzled
-  __shared__ uint32_t lds_st[kWaves][4][2][kStage];  // stage: [0] score bits, [1] (query tag, pool id)
+  __shared__ uint32_t lds_st[kWaves][kRB][2][kStage];  // stage: [0] score bits, [1] (query tag, pool id)
   __shared__ int lds_np[kWaves];
   __shared__ uint32_t lds_fail[kWaves];
   __shared__ int lds_tile;
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
   const float NEG_INF = -__builtin_huge_valf();
   const float POS_INF = __builtin_huge_valf();
   const int64_t nrow = kTwoPhase ? a.Sq : (int64_t)__builtin_amdgcn_readfirstlane(*a.nrows);
-  const int64_t ntiles = (nrow + kQT - 1) / kQT;
+  const int64_t ntiles = (nrow + kQTile - 1) / kQTile;
   const uint32_t lane_tag = ((uint32_t)g << kTagShift) | (uint32_t)c16;
   int dma_off[2];  // byte offset in a key tile of the chunk this thread's loads bring
 #pragma unroll
@@ -336,22 +341,22 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
   for (;;) {
     const int64_t rank = lds_tile;
     if (rank >= ntiles) break;
-    const int64_t q0 = (kTwoPhase ? ntiles - 1 - rank : rank) * kQT;
+    const int64_t q0 = (kTwoPhase ? ntiles - 1 - rank : rank) * kQTile;
     auto row_of = [&](int64_t i) -> int64_t {
       if (i >= nrow) return -1;
       return kTwoPhase ? i : (int64_t)a.rows[i];
     };
 
-    // A operands: row (4*qq + h) of row block rb -> query 16*wave + 4*rb + qq,
+    // A operands: row (4*qq + h) of row block rb -> query kQW*wave + 4*rb + qq,
     // head h, weight folded in.  cl[rb][h]: the clamp side of the lane's query
     // (row block rb, query g) and head h.
-    bf16x8_t A[4][2];
-    float cl[4][4];
-    int nc[4];
+    bf16x8_t A[kRB][2];
+    float cl[kRB][4];
+    int nc[kRB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       {
-        const int64_t qr = row_of(q0 + 16 * wave + 4 * rb + (c16 >> 2));
+        const int64_t qr = row_of(q0 + kQW * wave + 4 * rb + (c16 >> 2));
         const int h = c16 & 3;
         const bool ok = qr >= 0 && h < a.heads;
         const uint16_t* src = a.q_idx + (qr * a.heads + h) * kDI + 8 * g;
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
                          : zero_bf16x8();
       }
       {
-        const int64_t qr = row_of(q0 + 16 * wave + 4 * rb + g);
+        const int64_t qr = row_of(q0 + kQW * wave + 4 * rb + g);
         const bool ok = qr >= 0;
         int64_t pos = 0;
         if (ok) {
@@ -377,22 +382,29 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         }
       }
     }
-    int ncm = max(max(nc[0], nc[1]), max(nc[2], nc[3]));
+    int ncm = nc[0];
+#pragma unroll
+    for (int rb = 1; rb < kRB; ++rb) ncm = max(ncm, nc[rb]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ncm = max(ncm, __shfl_xor(ncm, o, kWave));
-    int ncmin = min(min(nc[0], nc[1]), min(nc[2], nc[3]));
+    int ncmin = nc[0];
+#pragma unroll
+    for (int rb = 1; rb < kRB; ++rb) ncmin = min(ncmin, nc[rb]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ncmin = min(ncmin, __shfl_xor(ncmin, o, kWave));
     ncmin = uniform(ncmin);
     if (lane == 0) lds_np[wave] = ncm;
     lds_barrier();
     if (tid == 0) lds_tile = (int)atomicAdd(a.tile_next, 1u);  // read after the tile
-    const int tp = max(max(lds_np[0], lds_np[1]), max(lds_np[2], lds_np[3]));
+    int tp = lds_np[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) tp = max(tp, lds_np[w]);
     const int ntp = (tp + kPT - 1) / kPT;   // pool tiles in the tile's causal range
 
-    float tau[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-    float tau2[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};  // the retry's thresholds
-    const int64_t wbase = ((int64_t)blockIdx.x * kQT + 16 * wave) * cap;
+    float tau[kRB], tau2[kRB];  // running thresholds, and the retry's
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) tau[rb] = tau2[rb] = NEG_INF;
+    const int64_t wbase = ((int64_t)blockIdx.x * kQTile + kQW * wave) * cap;
 
     // Pool-key tiles go straight from HBM to LDS (buffer loads with the LDS
     // destination) through a ring of kRing buffers, issued two tiles ahead of
@@ -442,22 +454,22 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         lbuf = lbuf == kRing - 1 ? 0 : lbuf + 1;
 
         // 16 output blocks of 16 (query x head) rows x 16 pools
-        f32x4_t acc[4][4];
+        f32x4_t acc[kRB][4];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const int pr = 16 * cb + c16;
           const bf16x8_t B0 = as_bf16x8(kb[pr * 8 + (g ^ (pr & 7))]);
           const bf16x8_t B1 = as_bf16x8(kb[pr * 8 + ((4 + g) ^ (pr & 7))]);
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
+          for (int rb = 0; rb < kRB; ++rb) {
             f32x4_t z = {0.f, 0.f, 0.f, 0.f};
             acc[rb][cb] = mfma32(A[rb][1], B1, mfma32(A[rb][0], B0, z));
           }
         }
         // epilogue: clamp each head to the side of its weight, sum the heads
-        float sc[4][4];
+        float sc[kRB][4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const f32x4_t x = acc[rb][cb];
@@ -471,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
         // causal pool mask, only on tiles some query of the wave sees in part
         if (pt0 + kPT > ncmin) {
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
+          for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
               if (pt0 + 16 * cb + c16 >= nc[rb]) sc[rb][cb] = NEG_INF;
@@ -486,9 +498,9 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       // Phase 1: each lane keeps, per query, the 8 best sampled scores of
       // its pool column (descending, in registers).  Their union holds at
       // most every sampled score, so its r-th best is at most the sample's.
-      int rq[2][4];
+      int rq[2][kRB];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         // r from the fraction f of the query's causal pools the sample
         // covers; 0 = no estimate (threshold stays -inf)
         const int n_full = nc[rb] / kPT, part = nc[rb] % kPT;
@@ -507,23 +519,23 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
           rq[m][rb] = r;
         }
       }
-      float best[4][kSampleKeep];
+      float best[kRB][kSampleKeep];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int j = 0; j < kSampleKeep; ++j) best[rb][j] = NEG_INF;
       // Per tile and query the lane's 4 new scores are sorted (5 exchanges),
       // merged into the 8 kept ones by taking the larger of kept[4+j] and
       // new[3-j] (the top 8 of the union, in bitonic order), and the 8 are
       // sorted again by a bitonic half-cleaner network (3 x 4 exchanges).
-      stream(0, kSampleStride, [](int) {}, [&](float (&sc)[4][4], int) {
+      stream(0, kSampleStride, [](int) {}, [&](float (&sc)[kRB][4], int) {
         auto cx = [](float& hi, float& lo) {
           const float h = fmaxf(hi, lo);
           lo = fminf(hi, lo);
           hi = h;
         };
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
           float n0 = sc[rb][0], n1 = sc[rb][1], n2 = sc[rb][2], n3 = sc[rb][3];
           cx(n0, n1); cx(n2, n3); cx(n0, n2); cx(n1, n3); cx(n1, n2);
           float* b = best[rb];
@@ -541,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       // r-th best of the 16 lanes x kSampleKeep kept scores of each query:
       // the largest key v with at least r kept keys >= v, bit by bit
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         uint32_t kk[kSampleKeep];
 #pragma unroll
         for (int j = 0; j < kSampleKeep; ++j) kk[j] = order_key(best[rb][j] + 0.f);
@@ -574,16 +586,18 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
     // pass once more, for those queries only, with the larger margin
     // (threshold +inf for the others); `redo` holds the wave's queries
     // (bit 4*rb + t) scored in the current attempt.
-    uint32_t redo = 0xFFFFu;
+    uint32_t redo = kQW >= 32 ? 0xFFFFFFFFu : (1u << kQW) - 1u;
 #pragma unroll 1
     for (int attempt = 0;; ++attempt) {
       if (attempt > 0) {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < kRB; ++rb)
           tau[rb] = ((redo >> (4 * rb + g)) & 1u) ? tau2[rb] : POS_INF;
       }
-      int nst[4] = {0, 0, 0, 0};   // staged entries per row block (wave-uniform)
-      int cnt_v = 0;               // lane q < 16: list length of wave query q = 4*rb + t
+      int nst[kRB];                // staged entries per row block (wave-uniform)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) nst[rb] = 0;
+      int cnt_v = 0;               // lane q < kQW: list length of wave query q = 4*rb + t
 
       // Entry j of stage rb (of n) is moved to the list of its query; `c` holds
       // the 4 list lengths of the row block and advances (stable per query).
@@ -609,9 +623,9 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       // every flagged stage are read before any is placed, so one LDS latency
       // covers them all.
       auto flush = [&](uint32_t fl) {
-        uint32_t f0[4], i0[4];
+        uint32_t f0[kRB], i0[kRB];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
           f0[rb] = 0u;
           i0[rb] = 0u;
           if ((fl >> rb) & 1u) {
@@ -622,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
           }
         }
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
           if (!((fl >> rb) & 1u)) continue;
           const int n = nst[rb];
           int c[4];
@@ -654,11 +668,14 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
             // kStage - 256 (the sign bit of count - (kStage - 255) is clear),
             // fl = counts > 0.
             const bool period = i > 0 && (i % kFlushPeriod) == 0;
-            if (!period && nst[0] + nst[1] + nst[2] + nst[3] <= kStage - 4 * kWave) return;
+            int nsum = 0;
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) nsum += nst[rb];
+            if (!period && nsum <= kStage - 4 * kWave) return;
             int neg = -1;
             uint32_t fl = 0;
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
+            for (int rb = 0; rb < kRB; ++rb) {
               neg &= nst[rb] - (kStage - 4 * kWave + 1);
               fl |= ((uint32_t)(-nst[rb]) >> 31) << rb;
             }
@@ -682,21 +699,21 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
                                                    lds_st[wave][rb][0], nullptr);
                 cnt_v = lane == q ? topk : cnt_v;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < kRB; ++r)
                   if (r == rb && g == tq) tau[r] = T;
               }
             }
           },
-          [&](float (&sc)[4][4], int pt0) {
+          [&](float (&sc)[kRB][4], int pt0) {
             // all 16 ballots come before the first branch on one of them, so
             // no branch waits on a compare issued just before it
-            uint64_t MM[4][4];
+            uint64_t MM[kRB][4];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+            for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
               for (int cb = 0; cb < 4; ++cb) MM[rb][cb] = ballot(sc[rb][cb] > tau[rb]);
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
+            for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
               for (int cb = 0; cb < 4; ++cb) {
                 const bool keep = sc[rb][cb] > tau[rb];
@@ -718,19 +735,21 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       {
         uint32_t fl = 0;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) fl |= nst[rb] > 0 ? 1u << rb : 0u;
+        for (int rb = 0; rb < kRB; ++rb) fl |= nst[rb] > 0 ? 1u << rb : 0u;
         if (fl) flush(fl);
       }
       __threadfence_block();
       uint32_t failed = 0;  // wave queries whose threshold was too high
 #pragma unroll 1
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < kQW; ++q) {
         if (!((redo >> q) & 1u)) continue;
-        const int64_t qr = row_of(q0 + 16 * wave + q);
+        const int64_t qr = row_of(q0 + kQW * wave + q);
         if (qr < 0) continue;
         const int rb = q >> 2;
         const int n = __builtin_amdgcn_readlane(cnt_v, q);
-        const int ncr = rb == 0 ? nc[0] : rb == 1 ? nc[1] : rb == 2 ? nc[2] : nc[3];
+        int ncr = nc[0];
+#pragma unroll
+        for (int r = 1; r < kRB; ++r) ncr = r == rb ? nc[r] : ncr;
         const int need = min(topk, __shfl(ncr, 16 * (q & 3), kWave));
         if (kTwoPhase && n < need) {  // threshold estimate too high
           if (attempt == 0) failed |= 1u << q;
@@ -764,7 +783,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a)
       if (!kTwoPhase || attempt > 0) break;
       if (lane == 0) lds_fail[wave] = failed;
       lds_barrier();
-      if ((lds_fail[0] | lds_fail[1] | lds_fail[2] | lds_fail[3]) == 0u) break;
+      uint32_t any_fail = 0u;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) any_fail |= lds_fail[w];
+      if (any_fail == 0u) break;
       redo = failed;
     }
     lds_barrier();  // publishes lds_tile; lds_np is reused in the next tile
@@ -778,6 +800,7 @@ struct Residency {
   int cus, per_cu;
 };
 
+template <int kRB>
 Residency index_residency() {
   static std::mutex mu;
   static Residency cache[64] = {};
@@ -788,8 +811,8 @@ Residency index_residency() {
   if (cache[dev].cus == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, indexer_topk_kernel<true>, kThreads, 0) !=
-            hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, indexer_topk_kernel<true, kRB>, kThreads,
+                                                     0) != hipSuccess ||
         cus * per <= 0) {
       (void)hipGetLastError();
       return fallback;
@@ -797,6 +820,47 @@ Residency index_residency() {
     cache[dev] = Residency{cus, per};
   }
   return cache[dev];
+}
+
+// Queries per wave.  16 (four row blocks) share each staged key tile among 64
+// queries of a workgroup; 4 (one row block) need 163 instead of 246 VGPRs, so a
+// CU holds three workgroups instead of two, and a short sequence yields four
+// times as many workgroups.  With 2^18 keys or fewer the pooled keys stay in
+// cache and the narrow variant is faster (1.15x at 2^17 and 2^18 keys, 2.9x at
+// 4096); at 2^20 keys the fourfold key traffic makes it 8% slower, and a grid
+// held to one workgroup a CU (CUs shared with the attention) wants the wide one.
+// DSA_INDEX_QUERIES_PER_WAVE=4 or 16 overrides the choice; both give the same ids.
+constexpr int64_t kIndexNarrowMaxKeys = int64_t(1) << 18;
+
+int index_queries_per_wave(const IndexArgs& ia) {
+  if (const char* e = std::getenv("DSA_INDEX_QUERIES_PER_WAVE")) {
+    if (std::strcmp(e, "4") == 0) return 4;
+    if (std::strcmp(e, "16") == 0) return 16;
+  }
+  return ia.Sk <= kIndexNarrowMaxKeys && ia.max_per_cu == 0 ? 4 : 16;
+}
+
+// Both passes with kRB row blocks (4 kRB queries) per wave.  The workspace
+// holds index_slots(Sq) x kIndexQueryTile candidate lists; a workgroup of this
+// variant owns kWaves x 4 kRB of them, so the grid never exceeds their count.
+template <int kRB>
+void launch_passes(KernelArgs a, const IndexArgs& ia, uint32_t* fb_count, hipStream_t s) {
+  constexpr int64_t qtile = (int64_t)kWaves * 4 * kRB;
+  const int64_t lists = index_slots(ia.Sq) * kIndexQueryTile;
+  int64_t slots = (ia.Sq + qtile - 1) / qtile;
+  if (slots > lists / qtile) slots = lists / qtile;
+  const Residency res = index_residency<kRB>();
+  const int per_cu = ia.max_per_cu > 0 && ia.max_per_cu < res.per_cu ? ia.max_per_cu : res.per_cu;
+  const int64_t resident = (int64_t)res.cus * per_cu;
+  if (resident < slots) slots = resident;
+  a.tile_next = fb_count + 1;
+  indexer_topk_kernel<true, kRB><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
+  // queries whose threshold estimate was too high twice, scored exactly.  They are
+  // rare (none to a few per 2^16 rows on the workloads); when other kernels share
+  // the CUs, a small grid finds free slots sooner than one workgroup per CU would.
+  a.tile_next = fb_count + 2;
+  const int64_t exact_slots = ia.max_per_cu > 0 && slots > kExactSharedSlots ? kExactSharedSlots : slots;
+  indexer_topk_kernel<false, kRB><<<dim3((unsigned)exact_slots), dim3(kThreads), 0, s>>>(a);
 }
 
 }  // namespace
@@ -833,19 +897,11 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   a.fb_rows = fb_rows;
   a.cand = reinterpret_cast<u32x2_t*>(ws + L.cand_off);
   a.idx_out = ia.idx_out;
-  int64_t slots = index_slots(ia.Sq);  // the workspace holds candidate lists for this many
-  const Residency res = index_residency();
-  const int per_cu = ia.max_per_cu > 0 && ia.max_per_cu < res.per_cu ? ia.max_per_cu : res.per_cu;
-  const int64_t resident = (int64_t)res.cus * per_cu;
-  if (resident < slots) slots = resident;
-  a.tile_next = fb_count + 1;
-  indexer_topk_kernel<true><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
-  // queries whose threshold estimate was too high twice, scored exactly.  They are
-  // rare (none to a few per 2^16 rows on the workloads); when other kernels share
-  // the CUs, a small grid finds free slots sooner than one workgroup per CU would.
-  a.tile_next = fb_count + 2;
-  const int64_t exact_slots = ia.max_per_cu > 0 && slots > kExactSharedSlots ? kExactSharedSlots : slots;
-  indexer_topk_kernel<false><<<dim3((unsigned)exact_slots), dim3(kThreads), 0, s>>>(a);
+  a.tile_next = nullptr;
+  if (index_queries_per_wave(ia) == 4)
+    launch_passes<1>(a, ia, fb_count, s);
+  else
+    launch_passes<4>(a, ia, fb_count, s);
   return hipGetLastError();
 }
 

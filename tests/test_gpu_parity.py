@@ -27,6 +27,15 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+@pytest.fixture(params=["4", "16"])
+def queries_per_wave(request, monkeypatch):
+    """Run an indexer test with both workgroup sub-tiles (16 and 64 queries).
+
+    The library picks one by key count; DSA_INDEX_QUERIES_PER_WAVE forces it."""
+    monkeypatch.setenv("DSA_INDEX_QUERIES_PER_WAVE", request.param)
+    return request.param
+
+
 def _bits(x):
     return syn.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
 
@@ -52,18 +61,18 @@ def gpu_index(q_idx, k_idx, w_idx, topk, q_chunk=256, q_pos=None):
 
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 7, 8, 63, 64, 65, 127, 200, 511, 515])
 @pytest.mark.parametrize("topk", [1, 3, 8, 64])
-def test_index_tiny_sweep(S, topk):
+def test_index_tiny_sweep(S, topk, queries_per_wave):
     q, k, w = _int_inputs(S, S, seed=S * 7 + topk)
-    note(f"index tiny S={S} topk={topk}")
+    note(f"index tiny S={S} topk={topk} qpw={queries_per_wave}")
     got = gpu_index(q, k, w, topk)
     ref = O.index_topk(q, k, w, None, topk, workers=1)
     assert_idx_equal(f"idx S={S} k={topk}", got, ref)
 
 
-def test_index_s4k_full():
+def test_index_s4k_full(queries_per_wave):
     wl = syn.WORKLOADS["s4k"]
     d = syn.make_inputs(wl, parts=("index",))
-    note("index s4k full")
+    note(f"index s4k full qpw={queries_per_wave}")
     got = gpu_index(d["q_idx"], d["k_idx"], d["w_idx"], wl.topk, wl.q_chunk)
     ref = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], None, wl.topk)
     assert_idx_equal("idx s4k", got, ref)
@@ -71,15 +80,15 @@ def test_index_s4k_full():
 
 @pytest.mark.parametrize("S,topk,heads", [(8192, 512, 4), (6000, 100, 3), (3001, 2048, 4),
                                           (2050, 17, 1)])
-def test_index_compaction_and_heads(S, topk, heads):
+def test_index_compaction_and_heads(S, topk, heads, queries_per_wave):
     q, k, w = _int_inputs(S, S, seed=S + topk, heads=heads)
-    note(f"index S={S} topk={topk} heads={heads}")
+    note(f"index S={S} topk={topk} heads={heads} qpw={queries_per_wave}")
     got = gpu_index(q, k, w, topk, q_chunk=512)
     ref = O.index_topk(q, k, w, None, topk)
     assert_idx_equal("idx", got, ref)
 
 
-def test_index_all_ties():
+def test_index_all_ties(queries_per_wave):
     S, topk = 2048, 40
     q, k, _ = _int_inputs(S, S, seed=3)
     w = _bits(np.zeros((S, 4)))
@@ -91,7 +100,7 @@ def test_index_all_ties():
 
 
 @pytest.mark.parametrize("direction", [1, -1])
-def test_index_monotone_scores(direction):
+def test_index_monotone_scores(direction, queries_per_wave):
     # score(p) = p (or n-1-p): with increasing scores every pool beats the
     # running threshold, so candidate lists fill and compact on every tile
     S, topk = 3072, 64
@@ -111,7 +120,7 @@ def test_index_monotone_scores(direction):
     assert got[last].tolist() == want.tolist()
 
 
-def test_index_chunk_invariance_repeat_and_positions():
+def test_index_chunk_invariance_repeat_and_positions(queries_per_wave):
     S, topk = 4096, 128
     q, k, w = _int_inputs(S, S, seed=11)
     base = gpu_index(q, k, w, topk, q_chunk=256)
@@ -125,7 +134,7 @@ def test_index_chunk_invariance_repeat_and_positions():
     assert_idx_equal("idx 4096", base, ref)
 
 
-def test_index_subset_positions_sk_larger():
+def test_index_subset_positions_sk_larger(queries_per_wave):
     # queries are a strided subset of a longer sequence (Sk not a multiple of 4)
     Sk, topk = 5003, 32
     pos = np.arange(0, Sk, 7)[::-1].copy()
@@ -158,7 +167,7 @@ def _threshold_trap_keys(S, unsampled):
 
 @pytest.mark.parametrize("unsampled", [125, 10])
 @pytest.mark.parametrize("permute", [False, True])
-def test_index_sampled_threshold_too_high(unsampled, permute):
+def test_index_sampled_threshold_too_high(unsampled, permute, queries_per_wave):
     # every query row needs its own fallback: a retry, or the exact pass; with
     # permuted positions a workgroup mixes rows that fail with rows that do not
     S, topk = 10240, 64
@@ -166,7 +175,7 @@ def test_index_sampled_threshold_too_high(unsampled, permute):
     q = _bits(np.ones((S, 4, 64), np.float32))
     w = _bits(np.ones((S, 4), np.float32))
     pos = np.random.default_rng(17).permutation(S) if permute else None
-    note(f"index threshold trap unsampled={unsampled} permute={permute}")
+    note(f"index threshold trap unsampled={unsampled} permute={permute} qpw={queries_per_wave}")
     got = gpu_index(q, k_idx, w, topk, q_pos=pos)
     ref = O.index_topk(q, k_idx, w, pos, topk)
     assert_idx_equal(f"idx trap {unsampled}", got, ref)
@@ -418,6 +427,7 @@ def test_full_size_backward_sampled_keys(name):
     (300_001, 300_001, 3, 32, False, False),     # 2 chunks, ragged tail tile
     (262_144, 1 << 20, 2, 16, True, False),      # zig-zag share: q_pos given, 2 chunks
     (1031, 1031, 5, 16, False, False),           # one chunk
+    (262_144, 262_144, 2, 16, False, False),     # 2 chunks: 16- then 64-query indexer sub-tiles
     (300_001, 300_001, 3, 32, False, True),      # aux stream == stream: sequential
 ])
 def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream):
