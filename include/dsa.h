@@ -108,13 +108,13 @@ const char* dsa_last_error(void);
  * q_chunk is the query chunk of the pages' indexer, there a bound on the
  * memory of materialised score rows.  No score row leaves the chip here, so
  * the chunk bounds nothing: it is validated (>= 1) and otherwise unused; the
- * kernel scores sub-tiles of 64 queries (16 when Sk <= 2^18) and the result
+ * kernel scores sub-tiles of 32 queries (16 when Sq <= 2^15) and the result
  * depends neither on q_chunk nor on the sub-tile.  The workspace (see
  * dsa_index_topk_ws_bytes) holds the pooled keys and fixed-size candidate
  * lists for at most 512 x 64 queries in flight.
- * Environment: DSA_INDEX_QUERIES_PER_WAVE=4 or 16, read at each call, forces
- * the 16- or the 64-query sub-tile (a tuning and test override; the ids are
- * the same).  Other values are ignored.
+ * Environment: DSA_INDEX_QUERIES_PER_WAVE=4, 8 or 16, read at each call,
+ * forces the 16-, 32- or 64-query sub-tile (a tuning and test override; the
+ * ids are the same).  Other values are ignored.
  */
 size_t dsa_index_topk_ws_bytes(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim,
                                int32_t pool, int32_t topk, int32_t q_chunk);

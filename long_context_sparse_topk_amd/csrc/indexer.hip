@@ -8,9 +8,9 @@
 //
 // Kernels:
 //   pool_keys_kernel    kpool[p] = bf16(mean of k_idx[4p..4p+3])   (HBM-bound)
-//   indexer_topk_kernel per workgroup sub-tile of 64 queries, 16 a wave (256
-//                       rows of query x indexer-head; 16 queries, 4 a wave, on
-//                       a short key range), stream the causal pool range in
+//   indexer_topk_kernel per workgroup sub-tile of 16, 32 or 64 queries (4 kRB
+//                       a wave, 4 rows of query x indexer-head per query),
+//                       stream the causal pool range in
 //                       tiles of 64 pools staged in LDS; bf16 MFMA 16x16x32 gives
 //                       the 4 head dot products of a (query, pool) pair in one
 //                       lane (head weights folded into the query operand), so
@@ -303,7 +303,7 @@ __device__ __forceinline__ bf16x8_t fold_weight(u32x4_t q, float w) {
 // order).  Keeping global stores out of the scoring loop keeps the prefetch
 // wait exact (loads and stores share one completion counter).
 template <bool kTwoPhase, int kRB>
-__global__ __launch_bounds__(kThreads, 2) void indexer_topk_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kernel(KernelArgs a) {
   constexpr int kQW = 4 * kRB;        // queries per wave (kRB row blocks of 4)
   constexpr int kQTile = kWaves * kQW;  // queries per workgroup tile
   __shared__ __align__(16) u32x4_t lds_k[kRing][kPT * 8];   // ring of (64 pools x 128 B), swizzled
@@ -822,22 +822,27 @@ Residency index_residency() {
   return cache[dev];
 }
 
-// Queries per wave.  16 (four row blocks) share each staged key tile among 64
-// queries of a workgroup; 4 (one row block) need 163 instead of 246 VGPRs, so a
-// CU holds three workgroups instead of two, and a short sequence yields four
-// times as many workgroups.  With 2^18 keys or fewer the pooled keys stay in
-// cache and the narrow variant is faster (1.15x at 2^17 and 2^18 keys, 2.9x at
-// 4096); at 2^20 keys the fourfold key traffic makes it 8% slower, and a grid
-// held to one workgroup a CU (CUs shared with the attention) wants the wide one.
-// DSA_INDEX_QUERIES_PER_WAVE=4 or 16 overrides the choice; both give the same ids.
-constexpr int64_t kIndexNarrowMaxKeys = int64_t(1) << 18;
+// Queries per wave, 4 kRB.  kRB = 4 shares each staged key tile among 64
+// queries of a workgroup but needs 246 VGPRs and 81 KB of LDS: two workgroups
+// a CU.  kRB = 2 is held to 168 VGPRs (a few values spill) and needs 53 KB, so
+// a CU holds three; kRB = 1 needs 163 VGPRs and 39 KB, also three, in half-size
+// workgroups.  Measured per call, same ids: at S = 2^20 keys 85.0 ms for kRB = 2
+// against 98.3 (kRB = 4) and 106.4 (kRB = 1); at 2^17 keys 2.18 against 2.69
+// and 2.49 ms; at 2^15 and 4096 queries kRB = 1 is fastest (0.46 against 0.64
+// ms, 0.086 against 0.14), its grid of 16-query tiles filling the CUs evenly.
+// A grid held to one workgroup a CU (CUs shared with the attention forward)
+// runs best with kRB = 4 (a pipelined S = 2^20 call: 201 ms, 240 with kRB = 2).
+// DSA_INDEX_QUERIES_PER_WAVE=4, 8 or 16 overrides the choice; all give the same ids.
+constexpr int64_t kIndexNarrowMaxQueries = int64_t(1) << 15;
 
 int index_queries_per_wave(const IndexArgs& ia) {
   if (const char* e = std::getenv("DSA_INDEX_QUERIES_PER_WAVE")) {
     if (std::strcmp(e, "4") == 0) return 4;
+    if (std::strcmp(e, "8") == 0) return 8;
     if (std::strcmp(e, "16") == 0) return 16;
   }
-  return ia.Sk <= kIndexNarrowMaxKeys && ia.max_per_cu == 0 ? 4 : 16;
+  if (ia.max_per_cu > 0) return 16;
+  return ia.Sq <= kIndexNarrowMaxQueries ? 4 : 8;
 }
 
 // Both passes with kRB row blocks (4 kRB queries) per wave.  The workspace
@@ -898,10 +903,11 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   a.cand = reinterpret_cast<u32x2_t*>(ws + L.cand_off);
   a.idx_out = ia.idx_out;
   a.tile_next = nullptr;
-  if (index_queries_per_wave(ia) == 4)
-    launch_passes<1>(a, ia, fb_count, s);
-  else
-    launch_passes<4>(a, ia, fb_count, s);
+  switch (index_queries_per_wave(ia)) {
+    case 4: launch_passes<1>(a, ia, fb_count, s); break;
+    case 8: launch_passes<2>(a, ia, fb_count, s); break;
+    default: launch_passes<4>(a, ia, fb_count, s); break;
+  }
   return hipGetLastError();
 }
 

@@ -27,11 +27,11 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["4", "16"])
+@pytest.fixture(params=["4", "8", "16"])
 def queries_per_wave(request, monkeypatch):
-    """Run an indexer test with both workgroup sub-tiles (16 and 64 queries).
+    """Run an indexer test with each workgroup sub-tile (16, 32 and 64 queries).
 
-    The library picks one by key count; DSA_INDEX_QUERIES_PER_WAVE forces it."""
+    The library picks one by query count and launch; DSA_INDEX_QUERIES_PER_WAVE forces it."""
     monkeypatch.setenv("DSA_INDEX_QUERIES_PER_WAVE", request.param)
     return request.param
 
@@ -427,7 +427,7 @@ def test_full_size_backward_sampled_keys(name):
     (300_001, 300_001, 3, 32, False, False),     # 2 chunks, ragged tail tile
     (262_144, 1 << 20, 2, 16, True, False),      # zig-zag share: q_pos given, 2 chunks
     (1031, 1031, 5, 16, False, False),           # one chunk
-    (262_144, 262_144, 2, 16, False, False),     # 2 chunks: 16- then 64-query indexer sub-tiles
+    (32_768 * 8, 32_768 * 8, 2, 16, False, False),  # 2 chunks: 32- then 64-query indexer sub-tiles
     (300_001, 300_001, 3, 32, False, True),      # aux stream == stream: sequential
 ])
 def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream):
