@@ -175,7 +175,8 @@ int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32
  * aux_stream == stream the two stages run one after the other on `stream`.
  * The call creates its events (one per chunk, at most 7) and destroys them
  * before returning; the runtime releases each once it has completed.
- * Chunks: about one per 2^17 query rows, at most 6, of equal indexer work.
+ * Chunks: about one per 2^17 query rows, at most 6; the first holds 3/4 of
+ * an equal share of the indexer work, the others equal shares.
  */
 size_t dsa_index_attn_fwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim,
                                    int32_t pool, int32_t topk, int32_t q_chunk);

@@ -450,7 +450,7 @@ def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream):
     assert torch.equal(out_p, out_s), "pipelined out differs from dsa_sparse_attn_fwd"
     assert torch.equal(lse_p, lse_s), "pipelined lse differs from dsa_sparse_attn_fwd"
     # and the oracle on sampled rows, chunk boundaries included
-    bounds = [int(round(Sq * np.sqrt(c / 2) / 64)) * 64 for c in (1,)]
+    bounds = [int(round(Sq * np.sqrt(0.75 / 2) / 64)) * 64]   # the one inner boundary of 2 chunks
     rows = np.unique(np.concatenate([sample_rows(Sq, topk, pos, n_random=24),
                                      [b + d for b in bounds for d in (-1, 0, 1) if 0 <= b + d < Sq]]))
     ref_idx = O.index_topk(qi, ki, wi, pos, topk, rows=rows)
