@@ -10,7 +10,7 @@ line: tokens/s of the primary workload over the timed steps, the roofline of
 its dominant kernel (per-launch durations from HIP events on the launch stream,
 in a pass of the separate entry points after the timed steps), the CPU oracle
 timed on a bounded sample of the same workload, and the secondary workload's
-tokens/s.
+tokens/s, with the autograd integration's modes (plain, lean, offload) timed on it.
 """
 from __future__ import annotations
 
@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import long_context_sparse_topk_amd as D  # noqa: E402
+from long_context_sparse_topk_amd import training as TR  # noqa: E402
 import synthetic as syn  # noqa: E402
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
@@ -191,6 +192,33 @@ def run(layer: Layer, steps: int, warmup: int):
     return wall, avg, avg_step
 
 
+def training_modes(layer: Layer, steps: int, warmup: int):
+    """The autograd integration on the same inputs, per mode: ms per step (forward and
+    backward, wall clock between synchronisations) and the bytes the layer keeps between
+    its forward and its backward beyond its own inputs (device) or in pinned host memory."""
+    t, wl = layer.t, layer.wl
+    q, k, v = (t[n].detach().requires_grad_(True) for n in ("q", "k", "v"))
+    res = {}
+    for mode in TR.MODES:
+        def step():
+            out, _ = TR.sparse_attention(t["q_idx"], t["k_idx"], t["w_idx"], q, k, v, topk=wl.topk,
+                                         q_pos=layer.q_pos, scale=SCALE, q_chunk=wl.q_chunk, mode=mode)
+            kept = (out.grad_fn.saved_device_bytes, out.grad_fn.saved_host_bytes)
+            torch.autograd.grad(out, (q, k, v), t["dout"])
+            return kept
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            kept = step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        res[mode] = {"ms_per_step": round(ms, 3), "kept_device_bytes": int(kept[0]),
+                     "kept_host_bytes": int(kept[1])}
+    return res
+
+
 def source_hash(rel: str) -> str:
     h = hashlib.sha256()
     for f in (rel, "long_context_sparse_topk_amd/csrc/dsa_device.hpp",
@@ -322,6 +350,8 @@ def main():
         secondary["index_ws_bytes"] = int(sl.ws_idx.numel())
         if sw.backward:
             secondary["bwd_ws_bytes"] = int(sl.ws_bwd.numel())
+            log(f"{sw.name}: training modes (autograd)")
+            secondary["training"] = training_modes(sl, args.steps, args.warmup)
         del sl
 
     # the remaining workloads: throughput, the indexer's fraction of the MFMA peak and the

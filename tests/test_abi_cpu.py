@@ -200,3 +200,16 @@ def test_python_binding_checks_output_shapes():
         D.sparse_attn_bwd(q, k, v, q, q, torch.zeros(64, 3), idx)
     with pytest.raises(TypeError, match="ws must be"):
         D.index_topk(qi, ki, wi, topk=8, ws=torch.zeros(1 << 20, dtype=torch.float32))
+
+
+def test_training_rejects_unknown_mode():
+    # the mode is checked before any library call
+    import torch
+    from long_context_sparse_topk_amd import training as T
+    bf = torch.bfloat16
+    qi, ki, wi = torch.zeros(8, 4, 64, dtype=bf), torch.zeros(8, 64, dtype=bf), torch.zeros(8, 4, dtype=bf)
+    q = torch.zeros(8, 2, 128, dtype=bf, requires_grad=True)
+    k, v = torch.zeros(8, 128, dtype=bf), torch.zeros(8, 128, dtype=bf)
+    assert T.MODES == ("plain", "lean", "offload")
+    with pytest.raises(ValueError, match="mode must be one of"):
+        T.sparse_attention(qi, ki, wi, q, k, v, topk=2, mode="recompute-all")
