@@ -40,8 +40,10 @@
  *     return without synchronising.  Inputs must stay valid until the stream
  *     has executed the call.
  *   - The caller allocates and owns every buffer, including workspaces; the
- *     library allocates no device memory, keeps no state between calls,
- *     never writes its inputs and overwrites its outputs completely.  Calls
+ *     library allocates no device memory, keeps no state between calls
+ *     beyond what dsa_set_index_queries_per_wave sets and the pipelined
+ *     call's reusable events, never writes its inputs and overwrites its
+ *     outputs completely.  Calls
  *     from several host threads are safe; two calls that share an output or
  *     workspace buffer on different streams race.
  *   - Arguments are validated on the host before any HIP call.  Unsupported
@@ -103,8 +105,13 @@ const char* dsa_last_error(void);
  *   idx_out [Sq, topk]               int32  output
  *   ws      workspace of ws_bytes >= dsa_index_topk_ws_bytes(...) bytes
  *
- * Supported: idx_dim == 64, 1 <= idx_heads <= 4, pool == 4,
- * 1 <= topk <= 2048, q_chunk >= 1, 1 <= Sq, 1 <= Sk < 2^31.
+ * Supported: idx_dim == 64, 1 <= idx_heads <= 8, pool == 4,
+ * 1 <= topk <= 2048, q_chunk >= 1, 1 <= Sq, 1 <= Sk < 2^31.  (The MFMA tile
+ * holds 4 heads of each query; 5 to 8 heads take two such groups.  topk is
+ * capped at 2048 pools (8195 keys a query, four times the pages' 2051)
+ * because the workspace keeps, for every query in flight (up to 512 x 64), a
+ * candidate list of about 3*topk + 440 entries of 8 bytes: 1.7 GB at 2048,
+ * growing linearly with topk.)
  * q_chunk is the query chunk of the pages' indexer, there a bound on the
  * memory of materialised score rows.  No score row leaves the chip here, so
  * the chunk bounds nothing: it is validated (>= 1) and otherwise unused; the
@@ -112,9 +119,6 @@ const char* dsa_last_error(void);
  * depends neither on q_chunk nor on the sub-tile.  The workspace (see
  * dsa_index_topk_ws_bytes) holds the pooled keys and fixed-size candidate
  * lists for at most 512 x 64 queries in flight.
- * Environment: DSA_INDEX_QUERIES_PER_WAVE=4, 8 or 16, read at each call,
- * forces the 16-, 32- or 64-query sub-tile (a tuning and test override; the
- * ids are the same).  Other values are ignored.
  */
 size_t dsa_index_topk_ws_bytes(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim,
                                int32_t pool, int32_t topk, int32_t q_chunk);
@@ -123,6 +127,14 @@ int dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_idx,
                    const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t idx_heads,
                    int32_t idx_dim, int32_t pool, int32_t topk, int32_t q_chunk,
                    int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Tuning override of the indexer's workgroup sub-tile, process-wide: 4, 8 or
+ * 16 queries per wave (16-, 32- or 64-query sub-tiles) for every later
+ * indexer launch, or 0 to let each call choose by its query count (the
+ * default).  The ids do not depend on it; it exists so that tests can run
+ * every sub-tile.  Takes effect for calls made after it returns; returns
+ * DSA_INVALID_ARG for other values. */
+int dsa_set_index_queries_per_wave(int32_t queries_per_wave);
 
 /* ---------------------------------------------------------------------------
  * Sparse attention forward.
@@ -140,8 +152,9 @@ int dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_idx,
  *   idx [Sq, topk] int32                q_pos [Sq] int32 or NULL
  *   out [Sq, heads, head_dim] bf16      lse [Sq, heads] fp32
  *
- * Supported: head_dim == 128, 1 <= heads <= 16, pool == 4,
+ * Supported: head_dim == 128, 1 <= heads <= 64, pool == 4,
  * 1 <= topk <= 2048, 1 <= Sq, 1 <= Sk < 2^31.  scale must be finite and > 0.
+ * (Heads go in groups of 16, one wave per query row and group.)
  */
 int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
                         const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads,
@@ -173,8 +186,9 @@ int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32
  * that chunk's indexer on `stream`, so it also sees all earlier work of
  * `stream`; earlier work of `aux_stream` stays ordered before it.  With
  * aux_stream == stream the two stages run one after the other on `stream`.
- * The call creates its events (one per chunk, at most 7) and destroys them
- * before returning; the runtime releases each once it has completed.
+ * The call orders the two streams with events that the library creates once
+ * per host thread and device (at most 7) and reuses on later calls; it
+ * allocates no device memory.
  * Chunks: about one per 2^17 query rows, at most 6; the first holds 3/4 of
  * an equal share of the indexer work, the others equal shares.
  */
@@ -192,12 +206,17 @@ int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx, 
  * Sparse attention backward.
  *
  * Gradients of L = sum(dout * O) for the forward above, with
- *   P = exp(scale * q.k - lse),  Delta[r,h] = sum_d dout[r,h,d] * out[r,h,d],
+ *   P = exp(scale * q.k - lse),  Delta[r,h] = sum_d dout[r,h,d] * O[r,h,d],
  *   dS = P * (dout.v - Delta),
  *   dq[r,h] = scale * sum_j dS_j k[j]
  *   dk[j]   = scale * sum_{r,h} dS q[r,h],  dv[j] = sum_{r,h} P dout[r,h]
  * All sums are fp32; dq, dk and dv are rounded to bf16 (nearest even) and
- * overwritten completely (0 for keys no row attends).  dq is computed per
+ * overwritten completely (0 for keys no row attends).  For dq, Delta is taken
+ * from `out` (the forward's bf16 O); for dk and dv it is summed in fp32 over
+ * the row's keys as sum_j P_j (dout . v[j]), which is the same quantity
+ * without the rounding of O to bf16 (dk sums many rows' dS, so that rounding
+ * would add up there).  P and dS enter the dk and dv products as a bf16 value
+ * plus its bf16 rounding remainder, which keeps their fp32 precision.  dq is computed per
  * query row; dk and dv per pool of 4 keys, over the query rows whose key set
  * holds the pool, found by inverting idx in the workspace (counting per
  * chunk of rows in LDS, no global atomics).  The order in which a pool's
@@ -223,6 +242,7 @@ int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
                         int32_t head_dim, int32_t pool, int32_t topk, float scale,
                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                         hipStream_t stream);
+
 
 #ifdef __cplusplus
 }  /* extern "C" */

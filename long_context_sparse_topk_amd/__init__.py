@@ -40,6 +40,7 @@ SIGNATURES = {
     "dsa_index_topk_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32, _I32]),
     "dsa_index_topk": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32,
                                       _P, _P, _SZ, _P]),
+    "dsa_set_index_queries_per_wave": (ctypes.c_int, [_I32]),
     "dsa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
                                            _F, _P, _P, _P]),
     "dsa_index_attn_fwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32, _I32]),
@@ -116,6 +117,18 @@ def _out(t, name: str, dtype: torch.dtype, shape: tuple, device: torch.device):
     return t
 
 
+def _kv_shapes(q, k, v):
+    """k and v must both be [Sk, D] with q's head_dim D: the kernels read K/V rows at that
+    stride, so any other width would send reads (and, in the backward, dk/dv writes) past
+    the end of the buffers."""
+    D = q.shape[2]
+    Sk = k.shape[0]
+    if tuple(k.shape) != (Sk, D) or tuple(v.shape) != (Sk, D):
+        raise ValueError(f"attention shapes disagree: k {tuple(k.shape)} and v {tuple(v.shape)} "
+                         f"must both be [Sk, {D}] (q's head_dim)")
+    return Sk
+
+
 def _positions(q_pos, Sq, device):
     if q_pos is None:
         return None
@@ -168,6 +181,13 @@ def index_topk(q_idx, k_idx, w_idx, *, topk: int, q_chunk: int = 256, q_pos=None
     return out
 
 
+def set_index_queries_per_wave(queries_per_wave: int) -> None:
+    """Force the indexer's workgroup sub-tile (4, 8 or 16 queries per wave) for every later
+    call in this process, or 0 to let each call choose (the default).  A tuning and test
+    setting: the selected ids do not depend on it."""
+    _check("dsa_set_index_queries_per_wave", lib().dsa_set_index_queries_per_wave(int(queries_per_wave)))
+
+
 def sparse_attn_fwd(q, k, v, idx, *, q_pos=None, scale: float | None = None, out=None, lse=None):
     """(out [Sq, H, 128] bf16, lse [Sq, H] fp32)."""
     L = lib()
@@ -177,9 +197,9 @@ def sparse_attn_fwd(q, k, v, idx, *, q_pos=None, scale: float | None = None, out
     _want(v, "v", torch.bfloat16, 2, dev)
     _want(idx, "idx", torch.int32, 2, dev)
     Sq, H, D = q.shape
-    Sk = k.shape[0]
-    if tuple(v.shape) != tuple(k.shape) or idx.shape[0] != Sq:
-        raise ValueError("attention shapes disagree")
+    Sk = _kv_shapes(q, k, v)
+    if idx.shape[0] != Sq:
+        raise ValueError("attention shapes disagree: idx must have Sq rows")
     q_pos = _positions(q_pos, Sq, dev)
     scale = default_scale(D) if scale is None else float(scale)
     out = torch.empty_like(q) if out is None else _out(out, "out", torch.bfloat16, (Sq, H, D), dev)
@@ -223,8 +243,8 @@ def index_attn_fwd(q_idx, k_idx, w_idx, q, k, v, *, topk: int, q_chunk: int = 25
     H, D = q.shape[1], q.shape[2]
     if k_idx.shape[1] != DI or tuple(w_idx.shape) != (Sq, HI):
         raise ValueError("indexer shapes disagree")
-    if q.shape[0] != Sq or tuple(v.shape) != tuple(k.shape) or k.shape[0] != Sk:
-        raise ValueError("attention shapes disagree")
+    if q.shape[0] != Sq or _kv_shapes(q, k, v) != Sk:
+        raise ValueError("attention shapes disagree: q must have Sq rows and k, v Sk rows")
     q_pos = _positions(q_pos, Sq, dev)
     scale = default_scale(D) if scale is None else float(scale)
     idx = (torch.empty((Sq, topk), dtype=torch.int32, device=dev) if idx is None
@@ -257,11 +277,11 @@ def sparse_attn_bwd(q, k, v, out, dout, lse, idx, *, q_pos=None, scale: float | 
     _want(lse, "lse", torch.float32, 2, dev)
     _want(idx, "idx", torch.int32, 2, dev)
     Sq, H, D = q.shape
-    Sk = k.shape[0]
+    Sk = _kv_shapes(q, k, v)
     q_pos = _positions(q_pos, Sq, dev)
     scale = default_scale(D) if scale is None else float(scale)
-    if tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != (Sq, H, D) or \
-            tuple(dout.shape) != (Sq, H, D) or tuple(lse.shape) != (Sq, H) or idx.shape[0] != Sq:
+    if tuple(out.shape) != (Sq, H, D) or tuple(dout.shape) != (Sq, H, D) or \
+            tuple(lse.shape) != (Sq, H) or idx.shape[0] != Sq:
         raise ValueError("attention shapes disagree")
     dq = torch.empty_like(q) if dq is None else _out(dq, "dq", torch.bfloat16, (Sq, H, D), dev)
     dk = torch.empty_like(k) if dk is None else _out(dk, "dk", torch.bfloat16, (Sk, D), dev)

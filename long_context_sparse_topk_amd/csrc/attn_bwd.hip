@@ -10,14 +10,16 @@
 //
 // Two passes, neither with atomics on the gradients:
 //
-//   dq pass (query-major): one wave per query row, four rows per workgroup,
-//     32 keys per tile, gathered from the row's idx list.  Also saves Delta.
+//   dq pass (query-major): one wave per (query row, group of 16 heads), four
+//     waves per workgroup, 32 keys per tile, gathered from the row's idx list.
+//     Also saves Delta.
 //       S^T  = K . Q^T,  dP^T = V . dO^T          MFMA 16x16x32, keys as M
 //       dQ^T += K^T dS^T                           MFMA 16x16x32, K^T read from LDS
 //
 //   dk/dv pass (pool-major): the idx lists are inverted first (count per
 //     pool, scan, scatter of the query rows), then one workgroup per pool of
-//     4 keys walks the rows that selected it, 16 (row, head) pairs per step:
+//     4 keys walks the rows that selected it, 16 (row, head) pairs per step
+//     (16/H whole rows when H <= 16, else 16 heads of one row):
 //       S  = Q . K^T,  dP = dO . V^T                MFMA 16x16x32, (row, head) as M,
 //                                                   the pool's keys as N (4 of 16)
 //       dK[key, dim] += dS^T Q,  dV += P^T dO       MFMA 16x16x16, (row, head) as k
@@ -51,7 +53,7 @@ struct BwdArgs {
   const int32_t* idx;
   const int32_t* q_pos;
   int64_t Sq, Sk;
-  int H, topk;
+  int H, HG, topk;         // heads, groups of 16 heads
   float scale, scale_log2;
   uint16_t* dq;
   float* stats;            // per (row, head): lse * log2(e), Delta, position (bits), 0
@@ -72,8 +74,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 
   const int lane = lane_id();
   const int wave = uniform(threadIdx.x >> 6);
-  const int64_t r = (int64_t)blockIdx.x * kRows + wave;
+  const int64_t item = (int64_t)blockIdx.x * kRows + wave;   // (row, head group)
+  const int64_t r = item / a.HG;
   if (r >= a.Sq) return;
+  const int h0 = 16 * (int)(item - r * a.HG);                 // first head of the group
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
@@ -91,12 +95,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int nps = np + (part > 0 ? 1 : 0);
   const int ntile = (nps + 7) >> 3;
 
-  // B operands with head c16: Q^T, dO^T; Delta from O
-  const bool hv = c16 < a.H;
+  // B operands with head h0 + c16: Q^T, dO^T; Delta from O
+  const int hd = h0 + c16;
+  const bool hv = hd < a.H;
   bf16x8_t QB[4], DB[4];
   float delta = 0.f;
   {
-    const int64_t off = (r * a.H + c16) * kD + 8 * g;
+    const int64_t off = (r * a.H + hd) * kD + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       QB[ks] = hv ? load_bf16x8(a.q + off + 32 * ks) : zero_bf16x8();
@@ -116,11 +121,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   }
   delta += __shfl_xor(delta, 16, kWave);
   delta += __shfl_xor(delta, 32, kWave);
-  const float lse2 = hv ? a.lse[r * a.H + c16] * kLog2e : 0.f;
-  if (hv && g == 0) {
-    f32x4_t rec = {lse2, delta, __int_as_float(pos), 0.f};
-    reinterpret_cast<f32x4_t*>(a.stats)[r * a.H + c16] = rec;
-  }
+  const float lse2 = hv ? a.lse[r * a.H + hd] * kLog2e : 0.f;
+  // Delta from the bf16 O serves this pass's dS.  The key loop also sums
+  // P_j dP_j = dO . (sum_j P_j V_j), Delta from the fp32 output the forward
+  // rounded; that value goes to the record that the dk/dv pass reads.
+  float dsum = 0.f;
 
   f32x4_t dqa[8];
 #pragma unroll
@@ -200,6 +205,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       for (int rr = 0; rr < 4; ++rr) {
         const float pp = (hv && rr < nv) ? exp2f(s[rr] * a.scale_log2 - lse2) : 0.f;
         ds[4 * kb + rr] = pp * (dp[rr] - delta);
+        dsum = fmaf(pp, dp[rr], dsum);
       }
     }
     u32x4_t dsb;
@@ -254,8 +260,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     compute(t + 1, B1);
   }
 
+  dsum += __shfl_xor(dsum, 16, kWave);
+  dsum += __shfl_xor(dsum, 32, kWave);
+  if (hv && g == 0) {
+    f32x4_t rec = {lse2, dsum, __int_as_float(pos), 0.f};
+    reinterpret_cast<f32x4_t*>(a.stats)[r * a.H + hd] = rec;
+  }
   if (hv) {
-    uint16_t* dst = a.dq + (r * a.H + c16) * kD + 4 * g;
+    uint16_t* dst = a.dq + (r * a.H + hd) * kD + 4 * g;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       u32x2_t o;
@@ -514,7 +526,7 @@ struct KvStep {
 __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvArgs a) {
   __shared__ __align__(16) uint16_t lds_q[kKvWaves][16 * kTStride];
   __shared__ __align__(16) uint16_t lds_do[kKvWaves][16 * kTStride];
-  __shared__ __align__(16) float lds_red[kKvWaves][2][4][kD];
+  __shared__ __align__(16) float lds_red[kKvWaves][2][8][kD];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -526,15 +538,38 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
   const int n = a.offs[p] - beg;
   const int64_t key0 = 4 * p;
   const int nkeys = a.Sk - key0 < 4 ? (int)(a.Sk - key0) : 4;
+  // A step holds 16 (row, head) pairs: with H <= 16, qpc = 16/H whole rows
+  // (nrh = qpc*H pairs used); with H > 16, heads 16c..16c+15 of one row, the
+  // row's cpr = ceil(H/16) groups in consecutive steps.
   const int H = a.H;
-  const int qpc = 16 / H;       // rows per step
-  const int nrh = qpc * H;      // (row, head) pairs per step
+  const bool wide = H > 16;
+  const int qpc = wide ? 1 : 16 / H;
+  const int nrh = wide ? 16 : qpc * H;
+  const int cpr = wide ? (H + 15) / 16 : 1;
+  // pair c of step s: the row's index in the chunk and its head; valid within H
+  auto pair_of = [&](int s, int c, int& j, int& h) -> bool {
+    if (wide) {
+      j = s / cpr;
+      h = 16 * (s - j * cpr) + c;
+      return h < H;
+    }
+    j = s * qpc + c / H;
+    h = c % H;
+    return c < nrh;
+  };
 
-  // K, V of the pool as B operands: B[dim 8g + j (+32 ks)][key c16], keys >= nkeys zero
+  // K, V of the pool as B operands: B[dim 8g + j (+32 ks)][column c16].  Columns
+  // 0-3 and 4-7 both hold the pool's keys 0-3 (zero past nkeys), 8-15 are zero.
+  // The dK/dV products take P and dS as bf16 operands; to keep their fp32
+  // precision each value v goes in as two bf16 parts, hi = bf16(v) in the
+  // row of columns 0-3 and lo = bf16(v - hi) in the row of columns 4-7, and
+  // the two output rows of a key are summed at the end.
+  const int kcol = c16 & 3;
+  const bool lo_lane = c16 >= 4 && c16 < 8;
   bf16x8_t KB[4], VB[4];
   {
-    const bool kv = c16 < nkeys;
-    const int64_t off = (key0 + c16) * kD + 8 * g;
+    const bool kv = c16 < 8 && kcol < nkeys;
+    const int64_t off = (key0 + kcol) * kD + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       KB[ks] = kv ? load_bf16x8(a.k + off + 32 * ks) : zero_bf16x8();
@@ -549,7 +584,7 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
   }
   uint16_t* tq = lds_q[wave];
   uint16_t* tdo = lds_do[wave];
-  const int64_t kpos = key0 + c16;   // key of this lane's D column
+  const int64_t kpos = key0 + kcol;  // key of this lane's D column
   const int toff = 4 * g * kTStride + tr_offset(c16, kTStride);
 
   // This wave's rows: a contiguous block of the pool's list, read 64 entries
@@ -559,10 +594,10 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
 
   // rows lst (lane j: entry j of the chunk), step s of the chunk, chunk length m
   auto load_step = [&](int lst, int s, int m, KvStep& o) {
-    const int ja = s * qpc + c16 / H;                   // A lanes: pair c16
-    const bool va = c16 < nrh && ja < m;
+    int ja, ha;
+    const bool va = pair_of(s, c16, ja, ha) && ja < m;  // A lanes: pair c16
     const int64_t ra = __shfl(lst, ja & 63, kWave);
-    const int64_t aoff = ((va ? ra : 0) * H + c16 % H) * kD + 8 * g;
+    const int64_t aoff = ((va ? ra : 0) * H + (va ? ha : 0)) * kD + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       o.q[ks] = va ? *reinterpret_cast<const u32x4_t*>(a.q + aoff + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
@@ -570,18 +605,17 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {                        // D lanes: pairs 4g + i
-      const int rh = 4 * g + i;
-      const int jd = s * qpc + rh / H;
-      const bool vr = rh < nrh && jd < m;
+      int jd, hdd;
+      const bool vr = pair_of(s, 4 * g + i, jd, hdd) && jd < m;
       const int64_t rd = __shfl(lst, jd & 63, kWave);
-      o.st[i] = vr ? a.stats[(vr ? rd : 0) * H + rh % H] : f32x4_t{0.f, 0.f, __int_as_float(-1), 0.f};
+      o.st[i] = vr ? a.stats[(vr ? rd : 0) * H + (vr ? hdd : 0)] : f32x4_t{0.f, 0.f, __int_as_float(-1), 0.f};
     }
   };
 
   for (int base = r0; base < r1; base += kWave) {
     const int m = min(kWave, r1 - base);
     const int lst = lane < m ? a.list[beg + base + lane] : 0;
-    const int nsteps = (m + qpc - 1) / qpc;
+    const int nsteps = wide ? m * cpr : (m + qpc - 1) / qpc;
     KvStep cur, nxt;
     load_step(lst, 0, m, cur);
     for (int s = 0; s < nsteps; ++s) {
@@ -601,16 +635,23 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
       float pv[4], dsv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = c16 < nkeys && kpos <= (int64_t)__float_as_int(cur.st[i][2]);
+        const bool ok = c16 < 8 && kcol < nkeys && kpos <= (int64_t)__float_as_int(cur.st[i][2]);
         pv[i] = ok ? exp2f(sv[i] * a.scale_log2 - cur.st[i][0]) : 0.f;
         dsv[i] = pv[i] * (dp[i] - cur.st[i][1]);
       }
-      // A operands of the 16x16x16 products: A[key c16][(row, head) 4g+j]
+      // A operands of the 16x16x16 products: A[column c16][(row, head) 4g+j],
+      // the bf16 value in columns 0-3 and its rounding remainder in 4-7
       u32x2_t pa, dsa;
       pa[0] = pack_bf16x2(pv[0], pv[1]);
       pa[1] = pack_bf16x2(pv[2], pv[3]);
       dsa[0] = pack_bf16x2(dsv[0], dsv[1]);
       dsa[1] = pack_bf16x2(dsv[2], dsv[3]);
+      if (lo_lane) {
+        pa[0] = pack_bf16x2(pv[0] - bf16_to_f32(pa[0] & 0xFFFFu), pv[1] - bf16_to_f32(pa[0] >> 16));
+        pa[1] = pack_bf16x2(pv[2] - bf16_to_f32(pa[1] & 0xFFFFu), pv[3] - bf16_to_f32(pa[1] >> 16));
+        dsa[0] = pack_bf16x2(dsv[0] - bf16_to_f32(dsa[0] & 0xFFFFu), dsv[1] - bf16_to_f32(dsa[0] >> 16));
+        dsa[1] = pack_bf16x2(dsv[2] - bf16_to_f32(dsa[1] & 0xFFFFu), dsv[3] - bf16_to_f32(dsa[1] >> 16));
+      }
       const s16x4_t PA = as_s16x4(pa), DSA = as_s16x4(dsa);
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -629,14 +670,15 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
     }
   }
 
-  // adk[db]: lane holds dK[key 4g+i][dim 16db+c16]; the pool's keys are in g == 0
-  if (g == 0) {
+  // adk[db]: lane holds row 4g+i, dim 16db+c16 of the product: the bf16 parts of
+  // key i in g == 0, the remainders of key i in g == 1
+  if (g < 2) {
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lds_red[wave][0][i][16 * db + c16] = adk[db][i];
-        lds_red[wave][1][i][16 * db + c16] = adv[db][i];
+        lds_red[wave][0][4 * g + i][16 * db + c16] = adk[db][i];
+        lds_red[wave][1][4 * g + i][16 * db + c16] = adv[db][i];
       }
   }
   __syncthreads();
@@ -651,7 +693,8 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
       for (int e = 0; e < 4; ++e) {
         float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < kKvWaves; ++w) acc += lds_red[w][which][key][d0 + e];
+        for (int w = 0; w < kKvWaves; ++w)
+          acc += lds_red[w][which][key][d0 + e] + lds_red[w][which][4 + key][d0 + e];
         v4[e] = which == 0 ? acc * a.scale : acc;
       }
       u32x2_t o;
@@ -710,12 +753,13 @@ hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s) {
   a.Sq = x.Sq;
   a.Sk = x.Sk;
   a.H = x.heads;
+  a.HG = (x.heads + 15) / 16;
   a.topk = x.topk;
   a.scale = x.scale;
   a.scale_log2 = x.scale * kLog2e;
   a.dq = x.out;
   a.stats = stats;
-  const int64_t blocks = (x.Sq + kRows - 1) / kRows;
+  const int64_t blocks = (x.Sq * a.HG + kRows - 1) / kRows;
   attn_bwd_dq_kernel<<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
 
   // dk, dv

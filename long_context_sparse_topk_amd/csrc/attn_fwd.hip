@@ -7,9 +7,11 @@
 // selected pools plus its own incomplete pool, all heads sharing one K/V head.
 // The softmax is accumulated tile by tile with a running max and sum.
 //
-// Mapping: one wave per query row, four rows per workgroup.  A tile is 8
-// pool slots = 32 keys.  Every gathered K/V row is a contiguous 256-byte
-// segment and every selected pool a contiguous 1 KiB segment of K (and of V).
+// Mapping: one wave per (query row, group of 16 heads), four waves per
+// workgroup; the groups of one row are neighbouring waves, so their K/V
+// gathers meet in the same caches.  A tile is 8 pool slots = 32 keys.  Every
+// gathered K/V row is a contiguous 256-byte segment and every selected pool a
+// contiguous 1 KiB segment of K (and of V).
 //   S^T[key, head] = K[key, :] . Q[head, :]      MFMA 16x16x32, keys as M
 //   O^T[dim, head] += V^T[dim, key] P^T[key, head]
 // The K rows are loaded straight into MFMA A-operand registers; V goes
@@ -34,7 +36,7 @@ struct FwdArgs {
   const int32_t* q_pos;
   int64_t q_base;  // position of row 0 when q_pos is NULL
   int64_t Sq, Sk;
-  int H, topk;
+  int H, HG, topk;         // heads, groups of 16 heads
   float scale_log2;
   uint16_t* out;
   float* lse;
@@ -65,8 +67,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
 
   const int lane = lane_id();
   const int wave = uniform(threadIdx.x >> 6);
-  const int64_t r = (int64_t)blockIdx.x * kRows + wave;
+  const int64_t item = (int64_t)blockIdx.x * kRows + wave;   // (row, head group)
+  const int64_t r = item / a.HG;
   if (r >= a.Sq) return;
+  const int h0 = 16 * (int)(item - r * a.HG);                 // first head of the group
   const int g = lane >> 4;
   const int c16 = lane & 15;
   const float NEG_INF = -__builtin_huge_valf();
@@ -88,10 +92,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   const int nps = np + (part > 0 ? 1 : 0);
   const int ntile = (nps + 7) >> 3;
 
-  const bool hv = c16 < a.H;
+  const int hd = h0 + c16;   // this lane's head
+  const bool hv = hd < a.H;
   bf16x8_t QB[4];
   {
-    const uint16_t* src = a.q + (r * a.H + c16) * kD + 8 * g;
+    const uint16_t* src = a.q + (r * a.H + hd) * kD + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) QB[ks] = hv ? load_bf16x8(src + 32 * ks) : zero_bf16x8();
   }
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   lt += __shfl_xor(lt, 32, kWave);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (hv) {
-    uint16_t* dst = a.out + (r * a.H + c16) * kD + 4 * g;
+    uint16_t* dst = a.out + (r * a.H + hd) * kD + 4 * g;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       u32x2_t o;
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
       o[1] = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
       *reinterpret_cast<u32x2_t*>(dst + 16 * db) = o;
     }
-    if (g == 0) a.lse[r * a.H + c16] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : NEG_INF;
+    if (g == 0) a.lse[r * a.H + hd] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : NEG_INF;
   }
 }
 
@@ -298,11 +303,12 @@ hipError_t launch_attn_fwd(const AttnArgs& x, hipStream_t s) {
   a.Sq = x.Sq;
   a.Sk = x.Sk;
   a.H = x.heads;
+  a.HG = (x.heads + 15) / 16;
   a.topk = x.topk;
   a.scale_log2 = x.scale * kLog2e;
   a.out = x.out;
   a.lse = x.lse_out;
-  const int64_t blocks = (x.Sq + kRows - 1) / kRows;
+  const int64_t blocks = (x.Sq * a.HG + kRows - 1) / kRows;
   if (x.fwd_shared)
     attn_fwd_kernel<false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
   else

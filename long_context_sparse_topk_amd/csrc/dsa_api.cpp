@@ -56,7 +56,8 @@ int check_attn_shape(int64_t Sq, int64_t Sk, int32_t heads, int32_t head_dim, in
   int st = check_seq(Sq, Sk, q_pos);
   if (st) return st;
   if (head_dim != 128) return fail(DSA_UNSUPPORTED_SHAPE, "head_dim=%d (supported: 128)", head_dim);
-  if (heads < 1 || heads > 16) return fail(DSA_UNSUPPORTED_SHAPE, "heads=%d (supported: 1..16)", heads);
+  if (heads < 1 || heads > dsa::kMaxHeads)
+    return fail(DSA_UNSUPPORTED_SHAPE, "heads=%d (supported: 1..%d)", heads, dsa::kMaxHeads);
   if (pool != 4) return fail(DSA_UNSUPPORTED_SHAPE, "pool=%d (supported: 4)", pool);
   if (topk < 1 || topk > dsa::kMaxTopk)
     return fail(DSA_UNSUPPORTED_SHAPE, "topk=%d (supported: 1..%d)", topk, dsa::kMaxTopk);
@@ -74,8 +75,8 @@ int check_index_shape(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim
   int st = check_seq(Sq, Sk, q_pos);
   if (st) return st;
   if (idx_dim != 64) return fail(DSA_UNSUPPORTED_SHAPE, "idx_dim=%d (supported: 64)", idx_dim);
-  if (idx_heads < 1 || idx_heads > 4)
-    return fail(DSA_UNSUPPORTED_SHAPE, "idx_heads=%d (supported: 1..4)", idx_heads);
+  if (idx_heads < 1 || idx_heads > dsa::kMaxIndexHeads)
+    return fail(DSA_UNSUPPORTED_SHAPE, "idx_heads=%d (supported: 1..%d)", idx_heads, dsa::kMaxIndexHeads);
   if (pool != 4) return fail(DSA_UNSUPPORTED_SHAPE, "pool=%d (supported: 4)", pool);
   if (topk < 1 || topk > dsa::kMaxTopk)
     return fail(DSA_UNSUPPORTED_SHAPE, "topk=%d (supported: 1..%d)", topk, dsa::kMaxTopk);
@@ -110,6 +111,31 @@ int64_t pipe_bound(int64_t Sq, int c, int n) {
   const double x = (double)Sq * std::sqrt(w);
   int64_t b = (int64_t)std::llround(x / dsa::kIndexQueryTile) * dsa::kIndexQueryTile;
   return b < 0 ? 0 : (b > Sq ? Sq : b);
+}
+
+// The pipelined call's events, created on first use per host thread and device
+// and reused by every later call of that thread: no runtime object is made on the
+// hot path, and calls from different threads never share an event (a wait takes
+// the state of the event's latest record, so sharing one across threads could
+// order a stream after another thread's work).  They live until the process ends.
+constexpr int kMaxDevices = 64;
+
+hipError_t pipe_events(int dev, hipEvent_t** out) {
+  thread_local hipEvent_t events[kMaxDevices][kPipeChunks + 1] = {};
+  thread_local bool made[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!made[dev]) {
+    for (int c = 0; c <= kPipeChunks; ++c) {
+      const hipError_t e = hipEventCreateWithFlags(&events[dev][c], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        for (int j = 0; j < c; ++j) (void)hipEventDestroy(events[dev][j]);
+        return e;
+      }
+    }
+    made[dev] = true;
+  }
+  *out = events[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -167,6 +193,13 @@ DSA_EXPORT int dsa_index_topk(const void* q_idx, const void* k_idx, const void* 
   a.idx_out = idx_out;
   a.ws = ws;
   return hip_status(dsa::launch_index_topk(a, stream), "dsa_index_topk launch");
+}
+
+DSA_EXPORT int dsa_set_index_queries_per_wave(int32_t queries_per_wave) {
+  g_err[0] = '\0';
+  if (!dsa::set_index_queries_per_wave(queries_per_wave))
+    return fail(DSA_INVALID_ARG, "queries_per_wave=%d (supported: 0, 4, 8, 16)", queries_per_wave);
+  return DSA_OK;
 }
 
 DSA_EXPORT int dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
@@ -239,15 +272,14 @@ DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const vo
 
   const int n = aux_stream == stream ? 1 : pipe_chunks(Sq);
   // events: one per chunk (indexer done) and one for the forward stream's end
-  hipEvent_t ev[kPipeChunks + 1] = {};
+  hipEvent_t* ev = nullptr;
   if (n > 1) {
-    for (int c = 0; c <= n; ++c) {
-      const hipError_t e = hipEventCreateWithFlags(&ev[c], hipEventDisableTiming);
-      if (e != hipSuccess) {
-        for (int j = 0; j < c; ++j) (void)hipEventDestroy(ev[j]);
-        (void)hipGetLastError();
-        return hip_status(e, "dsa_index_attn_fwd: hipEventCreateWithFlags");
-      }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = pipe_events(dev, &ev);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return hip_status(e, "dsa_index_attn_fwd: events");
     }
   }
   (void)hipGetLastError();
@@ -307,28 +339,24 @@ DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const vo
     // `stream` waits for the last forward chunk, so the caller can wait on it alone
     note(hipEventRecord(ev[n], aux_stream));
     note(hipStreamWaitEvent(stream, ev[n], 0));
-    // a recorded event may be destroyed before it completes; its resources are
-    // released once it has
-    for (int c = 0; c <= n; ++c) (void)hipEventDestroy(ev[c]);
   }
   return hip_status(err, "dsa_index_attn_fwd launch");
 }
 
 DSA_EXPORT size_t dsa_sparse_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t heads,
                                                int32_t head_dim, int32_t topk) {
-  if (Sq < 1 || Sk < 1 || head_dim != 128 || heads < 1 || heads > 16 || topk < 1 ||
+  if (Sq < 1 || Sk < 1 || head_dim != 128 || heads < 1 || heads > dsa::kMaxHeads || topk < 1 ||
       topk > dsa::kMaxTopk)
     return 0;
   return dsa::bwd_ws_layout(Sq, Sk, heads, topk).total;
 }
 
-DSA_EXPORT int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
-                                   const void* dout, const float* lse, const int32_t* idx,
-                                   const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads,
-                                   int32_t head_dim, int32_t pool, int32_t topk, float scale,
-                                   void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
-  g_err[0] = '\0';
+namespace {
+
+int check_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+              const float* lse, const int32_t* idx, const int32_t* q_pos, int64_t Sq, int64_t Sk,
+              int32_t heads, int32_t head_dim, int32_t pool, int32_t topk, float scale, void* dq,
+              void* dk, void* dv) {
   int st;
   if ((st = check_ptr(q, "q", 16))) return st;
   if ((st = check_ptr(k, "k", 16))) return st;
@@ -340,16 +368,18 @@ DSA_EXPORT int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, 
   if ((st = check_ptr(dq, "dq", 16))) return st;
   if ((st = check_ptr(dk, "dk", 16))) return st;
   if ((st = check_ptr(dv, "dv", 16))) return st;
-  if ((st = check_ptr(ws, "ws", 256))) return st;
   if ((st = check_attn_shape(Sq, Sk, heads, head_dim, pool, topk, scale, q_pos))) return st;
   // the inverted selection lists are indexed with 32-bit offsets
   if (Sq * (int64_t)(topk + 1) >= kMaxSeq)
     return fail(DSA_UNSUPPORTED_SHAPE, "Sq*(topk+1)=%lld must be < 2^31",
                 (long long)(Sq * (int64_t)(topk + 1)));
-  const size_t need = dsa::bwd_ws_layout(Sq, Sk, heads, topk).total;
-  if (ws_bytes < need) return fail(DSA_WORKSPACE_TOO_SMALL, "ws_bytes=%zu < %zu", ws_bytes, need);
+  return DSA_OK;
+}
 
-  (void)hipGetLastError();
+dsa::AttnArgs bwd_args(const void* q, const void* k, const void* v, const void* out,
+                       const void* dout, const float* lse, const int32_t* idx,
+                       const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads, int32_t topk,
+                       float scale, void* dq, void* dk, void* dv, void* ws) {
   dsa::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -368,5 +398,28 @@ DSA_EXPORT int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, 
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   a.ws = ws;
+  return a;
+}
+
+}  // namespace
+
+DSA_EXPORT int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, const int32_t* idx,
+                                   const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads,
+                                   int32_t head_dim, int32_t pool, int32_t topk, float scale,
+                                   void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  g_err[0] = '\0';
+  int st;
+  if ((st = check_bwd(q, k, v, out, dout, lse, idx, q_pos, Sq, Sk, heads, head_dim, pool, topk,
+                      scale, dq, dk, dv)))
+    return st;
+  if ((st = check_ptr(ws, "ws", 256))) return st;
+  const size_t need = dsa::bwd_ws_layout(Sq, Sk, heads, topk).total;
+  if (ws_bytes < need) return fail(DSA_WORKSPACE_TOO_SMALL, "ws_bytes=%zu < %zu", ws_bytes, need);
+
+  (void)hipGetLastError();
+  const dsa::AttnArgs a = bwd_args(q, k, v, out, dout, lse, idx, q_pos, Sq, Sk, heads, topk, scale,
+                                   dq, dk, dv, ws);
   return hip_status(dsa::launch_attn_bwd(a, stream), "dsa_sparse_attn_bwd launch");
 }

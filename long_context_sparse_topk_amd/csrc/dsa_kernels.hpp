@@ -12,6 +12,8 @@ constexpr int kIndexQueryTile = 64;     // queries per workgroup sub-tile
 constexpr int kIndexPoolTile = 64;      // pools per LDS-staged key tile
 constexpr int kIndexMaxSlots = 512;     // workgroups owning candidate lists (2 per CU x 256 CUs)
 constexpr int kMaxTopk = 2048;
+constexpr int kMaxIndexHeads = 8;       // indexer heads: one or two groups of 4 per query
+constexpr int kMaxHeads = 64;           // attention heads: groups of 16, one wave each
 // device counters at the head of the fallback region: [0] fallback-list
 // length, [1] and [2] the tile queues of the two-phase and the exact pass
 constexpr int kIndexCounters = 3;
@@ -75,6 +77,10 @@ struct IndexArgs {
 };
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
+
+// Process-wide override of the indexer's workgroup sub-tile (queries per wave 4, 8 or 16;
+// 0 = chosen per call).  Returns false for other values.
+bool set_index_queries_per_wave(int qpw);
 
 // ---- sparse attention --------------------------------------------------------
 struct AttnArgs {
@@ -141,5 +147,6 @@ inline BwdWorkspace bwd_ws_layout(int64_t Sq, int64_t Sk, int heads, int topk) {
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s);
+
 
 }  // namespace dsa

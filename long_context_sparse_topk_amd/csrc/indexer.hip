@@ -30,9 +30,8 @@
 // pool id" demands; compaction breaks score ties by list position, which is
 // pool order.
 
+#include <atomic>
 #include <cmath>
-#include <cstdlib>
-#include <cstring>
 #include <mutex>
 
 #include "dsa_device.hpp"
@@ -302,7 +301,7 @@ __device__ __forceinline__ bf16x8_t fold_weight(u32x4_t q, float w) {
 // per-query lists in HBM (stable per query, so each list stays in pool
 // order).  Keeping global stores out of the scoring loop keeps the prefetch
 // wait exact (loads and stores share one completion counter).
-template <bool kTwoPhase, int kRB>
+template <bool kTwoPhase, int kRB, int kHG>
 __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kernel(KernelArgs a) {
   constexpr int kQW = 4 * kRB;        // queries per wave (kRB row blocks of 4)
   constexpr int kQTile = kWaves * kQW;  // queries per workgroup tile
@@ -347,24 +346,25 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
       return kTwoPhase ? i : (int64_t)a.rows[i];
     };
 
-    // A operands: row (4*qq + h) of row block rb -> query kQW*wave + 4*rb + qq,
-    // head h, weight folded in.  cl[rb][h]: the clamp side of the lane's query
-    // (row block rb, query g) and head h.
-    bf16x8_t A[kRB][2];
-    float cl[kRB][4];
+    // A operands: row (4*qq + h) of row block rb and head group hg -> query
+    // kQW*wave + 4*rb + qq, head 4*hg + h, weight folded in.  cl[rb][hg][h]: the
+    // clamp side of the lane's query (row block rb, query g) and head 4*hg + h.
+    bf16x8_t A[kRB][kHG][2];
+    float cl[kRB][kHG][4];
     int nc[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      {
+#pragma unroll
+      for (int hg = 0; hg < kHG; ++hg) {
         const int64_t qr = row_of(q0 + kQW * wave + 4 * rb + (c16 >> 2));
-        const int h = c16 & 3;
+        const int h = 4 * hg + (c16 & 3);
         const bool ok = qr >= 0 && h < a.heads;
         const uint16_t* src = a.q_idx + (qr * a.heads + h) * kDI + 8 * g;
         const float wv = ok ? bf16_to_f32(a.w_idx[qr * a.heads + h]) : 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          A[rb][ks] = ok ? fold_weight(*reinterpret_cast<const u32x4_t*>(src + 32 * ks), wv)
-                         : zero_bf16x8();
+          A[rb][hg][ks] = ok ? fold_weight(*reinterpret_cast<const u32x4_t*>(src + 32 * ks), wv)
+                             : zero_bf16x8();
       }
       {
         const int64_t qr = row_of(q0 + kQW * wave + 4 * rb + g);
@@ -376,10 +376,13 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
         }
         nc[rb] = ok ? (int)((pos + 1) >> 2) : 0;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float wv = (ok && h < a.heads) ? bf16_to_f32(a.w_idx[qr * a.heads + h]) : 0.f;
-          cl[rb][h] = wv < 0.f ? NEG_INF : POS_INF;
-        }
+        for (int hg = 0; hg < kHG; ++hg)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const int hh = 4 * hg + h;
+            const float wv = (ok && hh < a.heads) ? bf16_to_f32(a.w_idx[qr * a.heads + hh]) : 0.f;
+            cl[rb][hg][h] = wv < 0.f ? NEG_INF : POS_INF;
+          }
       }
     }
     int ncm = nc[0];
@@ -453,18 +456,20 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
         buf = buf == kRing - 1 ? 0 : buf + 1;
         lbuf = lbuf == kRing - 1 ? 0 : lbuf + 1;
 
-        // 16 output blocks of 16 (query x head) rows x 16 pools
-        f32x4_t acc[kRB][4];
+        // 16 output blocks of 16 (query x head) rows x 16 pools per head group
+        f32x4_t acc[kRB][kHG][4];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const int pr = 16 * cb + c16;
           const bf16x8_t B0 = as_bf16x8(kb[pr * 8 + (g ^ (pr & 7))]);
           const bf16x8_t B1 = as_bf16x8(kb[pr * 8 + ((4 + g) ^ (pr & 7))]);
 #pragma unroll
-          for (int rb = 0; rb < kRB; ++rb) {
-            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            acc[rb][cb] = mfma32(A[rb][1], B1, mfma32(A[rb][0], B0, z));
-          }
+          for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int hg = 0; hg < kHG; ++hg) {
+              f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+              acc[rb][hg][cb] = mfma32(A[rb][hg][1], B1, mfma32(A[rb][hg][0], B0, z));
+            }
         }
         // epilogue: clamp each head to the side of its weight, sum the heads
         float sc[kRB][4];
@@ -472,12 +477,18 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
         for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            const f32x4_t x = acc[rb][cb];
-            const float s01 = __builtin_amdgcn_fmed3f(x[0], cl[rb][0], 0.f) +
-                              __builtin_amdgcn_fmed3f(x[1], cl[rb][1], 0.f);
-            const float s23 = __builtin_amdgcn_fmed3f(x[2], cl[rb][2], 0.f) +
-                              __builtin_amdgcn_fmed3f(x[3], cl[rb][3], 0.f);
-            sc[rb][cb] = s01 + s23;
+            float hs[kHG];
+#pragma unroll
+            for (int hg = 0; hg < kHG; ++hg) {
+              const f32x4_t x = acc[rb][hg][cb];
+              const float s01 = __builtin_amdgcn_fmed3f(x[0], cl[rb][hg][0], 0.f) +
+                                __builtin_amdgcn_fmed3f(x[1], cl[rb][hg][1], 0.f);
+              const float s23 = __builtin_amdgcn_fmed3f(x[2], cl[rb][hg][2], 0.f) +
+                                __builtin_amdgcn_fmed3f(x[3], cl[rb][hg][3], 0.f);
+              hs[hg] = s01 + s23;
+            }
+            if constexpr (kHG == 1) sc[rb][cb] = hs[0];
+            else sc[rb][cb] = hs[0] + hs[1];
           }
         }
         // causal pool mask, only on tiles some query of the wave sees in part
@@ -800,7 +811,7 @@ struct Residency {
   int cus, per_cu;
 };
 
-template <int kRB>
+template <int kRB, int kHG>
 Residency index_residency() {
   static std::mutex mu;
   static Residency cache[64] = {};
@@ -811,7 +822,7 @@ Residency index_residency() {
   if (cache[dev].cus == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, indexer_topk_kernel<true, kRB>, kThreads,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, indexer_topk_kernel<true, kRB, kHG>, kThreads,
                                                      0) != hipSuccess ||
         cus * per <= 0) {
       (void)hipGetLastError();
@@ -832,15 +843,15 @@ Residency index_residency() {
 // ms, 0.086 against 0.14), its grid of 16-query tiles filling the CUs evenly.
 // A grid held to one workgroup a CU (CUs shared with the attention forward)
 // runs best with kRB = 4 (a pipelined S = 2^20 call: 201 ms, 240 with kRB = 2).
-// DSA_INDEX_QUERIES_PER_WAVE=4, 8 or 16 overrides the choice; all give the same ids.
+// dsa_set_index_queries_per_wave(4, 8 or 16) overrides the choice (a tuning and
+// test setting, process-wide; all give the same ids).
 constexpr int64_t kIndexNarrowMaxQueries = int64_t(1) << 15;
 
+std::atomic<int> g_queries_per_wave{0};   // 0: chosen per call
+
 int index_queries_per_wave(const IndexArgs& ia) {
-  if (const char* e = std::getenv("DSA_INDEX_QUERIES_PER_WAVE")) {
-    if (std::strcmp(e, "4") == 0) return 4;
-    if (std::strcmp(e, "8") == 0) return 8;
-    if (std::strcmp(e, "16") == 0) return 16;
-  }
+  const int forced = g_queries_per_wave.load(std::memory_order_relaxed);
+  if (forced != 0) return forced;
   if (ia.max_per_cu > 0) return 16;
   return ia.Sq <= kIndexNarrowMaxQueries ? 4 : 8;
 }
@@ -848,27 +859,33 @@ int index_queries_per_wave(const IndexArgs& ia) {
 // Both passes with kRB row blocks (4 kRB queries) per wave.  The workspace
 // holds index_slots(Sq) x kIndexQueryTile candidate lists; a workgroup of this
 // variant owns kWaves x 4 kRB of them, so the grid never exceeds their count.
-template <int kRB>
+template <int kRB, int kHG>
 void launch_passes(KernelArgs a, const IndexArgs& ia, uint32_t* fb_count, hipStream_t s) {
   constexpr int64_t qtile = (int64_t)kWaves * 4 * kRB;
   const int64_t lists = index_slots(ia.Sq) * kIndexQueryTile;
   int64_t slots = (ia.Sq + qtile - 1) / qtile;
   if (slots > lists / qtile) slots = lists / qtile;
-  const Residency res = index_residency<kRB>();
+  const Residency res = index_residency<kRB, kHG>();
   const int per_cu = ia.max_per_cu > 0 && ia.max_per_cu < res.per_cu ? ia.max_per_cu : res.per_cu;
   const int64_t resident = (int64_t)res.cus * per_cu;
   if (resident < slots) slots = resident;
   a.tile_next = fb_count + 1;
-  indexer_topk_kernel<true, kRB><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
+  indexer_topk_kernel<true, kRB, kHG><<<dim3((unsigned)slots), dim3(kThreads), 0, s>>>(a);
   // queries whose threshold estimate was too high twice, scored exactly.  They are
   // rare (none to a few per 2^16 rows on the workloads); when other kernels share
   // the CUs, a small grid finds free slots sooner than one workgroup per CU would.
   a.tile_next = fb_count + 2;
   const int64_t exact_slots = ia.max_per_cu > 0 && slots > kExactSharedSlots ? kExactSharedSlots : slots;
-  indexer_topk_kernel<false, kRB><<<dim3((unsigned)exact_slots), dim3(kThreads), 0, s>>>(a);
+  indexer_topk_kernel<false, kRB, kHG><<<dim3((unsigned)exact_slots), dim3(kThreads), 0, s>>>(a);
 }
 
 }  // namespace
+
+bool set_index_queries_per_wave(int qpw) {
+  if (qpw != 0 && qpw != 4 && qpw != 8 && qpw != 16) return false;
+  g_queries_per_wave.store(qpw, std::memory_order_relaxed);
+  return true;
+}
 
 hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   const IndexWorkspace L = index_ws_layout(ia.Sq, ia.Sk, ia.topk);
@@ -903,10 +920,15 @@ hipError_t launch_index_topk(const IndexArgs& ia, hipStream_t s) {
   a.cand = reinterpret_cast<u32x2_t*>(ws + L.cand_off);
   a.idx_out = ia.idx_out;
   a.tile_next = nullptr;
-  switch (index_queries_per_wave(ia)) {
-    case 4: launch_passes<1>(a, ia, fb_count, s); break;
-    case 8: launch_passes<2>(a, ia, fb_count, s); break;
-    default: launch_passes<4>(a, ia, fb_count, s); break;
+  if (ia.heads > 4) {
+    // 5 to 8 indexer heads: two groups of 4 heads per query, 16-query sub-tile
+    launch_passes<1, 2>(a, ia, fb_count, s);
+  } else {
+    switch (index_queries_per_wave(ia)) {
+      case 4: launch_passes<1, 1>(a, ia, fb_count, s); break;
+      case 8: launch_passes<2, 1>(a, ia, fb_count, s); break;
+      default: launch_passes<4, 1>(a, ia, fb_count, s); break;
+    }
   }
   return hipGetLastError();
 }

@@ -52,6 +52,9 @@ def test_workspace_sizes():
     assert D.sparse_attn_bwd_ws_bytes(10, 1000, 4, 8) >= 4 * (10 * 4 + 250 + 10 * 9)
     assert D.sparse_attn_bwd_ws_bytes(131072, 131072, 4, 128) < 2**27
     assert D.lib().dsa_sparse_attn_bwd_ws_bytes(10, 1000, 4, 128, 0) == 0
+    # heads 1..64 are supported, 65 is not
+    assert D.sparse_attn_bwd_ws_bytes(10, 1000, 64, 8) >= 4 * (10 * 64 * 4)
+    assert D.lib().dsa_sparse_attn_bwd_ws_bytes(10, 1000, 65, 128, 8) == 0
 
 
 P = 1 << 20  # a fake, 16-byte aligned address: validation fails before any use
@@ -75,7 +78,8 @@ def _idx(**kw):
     (dict(q_pos=P + 2), 1, "q_pos is not 4-byte aligned"),
     (dict(Sk=1 << 31), 2, "< 2^31"),
     (dict(dim=128), 2, "idx_dim=128"),
-    (dict(heads=5), 2, "idx_heads=5"),
+    (dict(heads=9), 2, "idx_heads=9"),
+    (dict(heads=0), 2, "idx_heads=0"),
     (dict(pool=8), 2, "pool=8"),
     (dict(topk=0), 2, "topk=0"),
     (dict(topk=4096), 2, "topk=4096"),
@@ -102,7 +106,7 @@ def _fwd(**kw):
     (dict(lse=None), 1, "lse is NULL"),
     (dict(D=64), 2, "head_dim=64"),
     (dict(H=0), 2, "heads=0"),
-    (dict(H=17), 2, "heads=17"),
+    (dict(H=65), 2, "heads=65"),
     (dict(pool=2), 2, "pool=2"),
     (dict(topk=2049), 2, "topk=2049"),
     (dict(scale=0.0), 1, "scale"),
@@ -157,9 +161,9 @@ def _pipe(**kw):
     (dict(ws=None), 1, "ws is NULL"),
     (dict(Sq=65, Sk=64), 1, "Sq=65 > Sk=64"),
     (dict(DI=32), 2, "idx_dim=32"),
-    (dict(HI=5), 2, "idx_heads=5"),
+    (dict(HI=9), 2, "idx_heads=9"),
     (dict(D=64), 2, "head_dim=64"),
-    (dict(H=17), 2, "heads=17"),
+    (dict(H=65), 2, "heads=65"),
     (dict(topk=4096), 2, "topk=4096"),
     (dict(q_chunk=0), 1, "q_chunk=0"),
     (dict(scale=-1.0), 1, "scale"),
@@ -200,6 +204,26 @@ def test_python_binding_checks_output_shapes():
         D.sparse_attn_bwd(q, k, v, q, q, torch.zeros(64, 3), idx)
     with pytest.raises(TypeError, match="ws must be"):
         D.index_topk(qi, ki, wi, topk=8, ws=torch.zeros(1 << 20, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("width", [64, 256])
+@pytest.mark.parametrize("which", ["k", "v", "both"])
+def test_python_binding_checks_kv_width(width, which):
+    # K/V rows are read (and dK/dV rows written) at q's head_dim stride: a k or v of
+    # another width is rejected before any library call, in all three entry points
+    import torch
+    bf = torch.bfloat16
+    qi, ki, wi = torch.zeros(64, 4, 64, dtype=bf), torch.zeros(64, 64, dtype=bf), torch.zeros(64, 4, dtype=bf)
+    q = torch.zeros(64, 2, 128, dtype=bf)
+    k = torch.zeros(64, width if which in ("k", "both") else 128, dtype=bf)
+    v = torch.zeros(64, width if which in ("v", "both") else 128, dtype=bf)
+    idx = torch.zeros(64, 8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="must both be"):
+        D.sparse_attn_fwd(q, k, v, idx)
+    with pytest.raises(ValueError, match="must both be"):
+        D.index_attn_fwd(qi, ki, wi, q, k, v, topk=8)
+    with pytest.raises(ValueError, match="must both be"):
+        D.sparse_attn_bwd(q, k, v, q, q, torch.zeros(64, 2), idx)
 
 
 def test_training_rejects_unknown_mode():
