@@ -243,6 +243,27 @@ int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Sparse attention backward without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving or
+ * training loops that forbid allocation).
+ *
+ * Computes exactly what dsa_sparse_attn_bwd computes, with the same
+ * arguments less ws and ws_bytes, and allocates nothing: its workspace is a
+ * 96 MiB (100,663,296-byte) array in device memory that the library holds
+ * on every GPU it runs on until the process ends (its device address is
+ * looked up once per device, on the first call there).  Shapes whose
+ * workspace, dsa_sparse_attn_bwd_ws_bytes(...), exceeds 96 MiB return
+ * DSA_UNSUPPORTED_SHAPE before any HIP call (S = 131,072 with 4 heads and
+ * topk 128 needs 88.6 MiB).  All calls on one GPU share that array: two
+ * calls whose executions overlap on one GPU (different streams, or several
+ * host threads) race and give wrong gradients; order them on one stream.
+ */
+int dsa_sparse_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, const int32_t* idx,
+                                const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t heads,
+                                int32_t head_dim, int32_t pool, int32_t topk, float scale,
+                                void* dq, void* dk, void* dv, hipStream_t stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -49,6 +49,8 @@ SIGNATURES = {
     "dsa_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
     "dsa_sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32,
                                            _I32, _I32, _F, _P, _P, _P, _P, _SZ, _P]),
+    "dsa_sparse_attn_bwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32,
+                                                   _I32, _I32, _I32, _F, _P, _P, _P, _P]),
 }
 
 
@@ -296,4 +298,32 @@ def sparse_attn_bwd(q, k, v, out, dout, lse, idx, *, q_pos=None, scale: float | 
                                _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(dev))
     _check("dsa_sparse_attn_bwd", st)
+    return dq, dk, dv
+
+
+def sparse_attn_bwd_noalloc(q, k, v, out, dout, lse, idx, *, q_pos=None, scale: float | None = None,
+                            dq=None, dk=None, dv=None):
+    """sparse_attn_bwd without a workspace: the library uses its own device-resident scratch
+    (at most 96 MiB of workspace), so the call allocates nothing when dq, dk and dv are
+    given.  Calls that overlap on one GPU race (they share the scratch)."""
+    L = lib()
+    dev = q.device
+    for t, n, nd in ((q, "q", 3), (k, "k", 2), (v, "v", 2), (out, "out", 3), (dout, "dout", 3)):
+        _want(t, n, torch.bfloat16, nd, dev)
+    _want(lse, "lse", torch.float32, 2, dev)
+    _want(idx, "idx", torch.int32, 2, dev)
+    Sq, H, D = q.shape
+    Sk = _kv_shapes(q, k, v)
+    q_pos = _positions(q_pos, Sq, dev)
+    scale = default_scale(D) if scale is None else float(scale)
+    if tuple(out.shape) != (Sq, H, D) or tuple(dout.shape) != (Sq, H, D) or \
+            tuple(lse.shape) != (Sq, H) or idx.shape[0] != Sq:
+        raise ValueError("attention shapes disagree")
+    dq = torch.empty_like(q) if dq is None else _out(dq, "dq", torch.bfloat16, (Sq, H, D), dev)
+    dk = torch.empty_like(k) if dk is None else _out(dk, "dk", torch.bfloat16, (Sk, D), dev)
+    dv = torch.empty_like(v) if dv is None else _out(dv, "dv", torch.bfloat16, (Sk, D), dev)
+    st = L.dsa_sparse_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                       _ptr(idx), _ptr(q_pos), Sq, Sk, H, D, POOL, idx.shape[1], scale,
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _stream(dev))
+    _check("dsa_sparse_attn_bwd_noalloc", st)
     return dq, dk, dv

@@ -30,6 +30,8 @@
 //   The order in which a pool's rows are summed follows the scatter (device
 //   atomics), so it is not fixed.
 
+#include <mutex>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -779,6 +781,40 @@ hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s) {
   kv.dv = x.dv;
   attn_bwd_dkdv_kernel<<<dim3((unsigned)np), dim3(kKvWaves * kWave), 0, s>>>(kv);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the workspace is a file-scope device array, one copy
+// per GPU, that lives until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in symbol): its
+// device address is looked up once per device with hipGetSymbolAddress and
+// that address is what the kernels receive.  Nothing in the workspace has to
+// start at zero (every pass writes what a later pass reads), so it is not
+// cleared.  All calls on one GPU share the array: calls that overlap on a GPU
+// (on different streams) race.
+
+namespace {
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+constexpr int kScratchDevices = 64;
+}  // namespace
+
+hipError_t bwd_scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dsa

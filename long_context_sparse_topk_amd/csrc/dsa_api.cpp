@@ -423,3 +423,32 @@ DSA_EXPORT int dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                                    dq, dk, dv, ws);
   return hip_status(dsa::launch_attn_bwd(a, stream), "dsa_sparse_attn_bwd launch");
 }
+
+DSA_EXPORT int dsa_sparse_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                                           const void* out, const void* dout, const float* lse,
+                                           const int32_t* idx, const int32_t* q_pos, int64_t Sq,
+                                           int64_t Sk, int32_t heads, int32_t head_dim,
+                                           int32_t pool, int32_t topk, float scale, void* dq,
+                                           void* dk, void* dv, hipStream_t stream) {
+  g_err[0] = '\0';
+  int st;
+  if ((st = check_bwd(q, k, v, out, dout, lse, idx, q_pos, Sq, Sk, heads, head_dim, pool, topk,
+                      scale, dq, dk, dv)))
+    return st;
+  const size_t need = dsa::bwd_ws_layout(Sq, Sk, heads, topk).total;
+  if (need > dsa::kBwdScratchBytes)
+    return fail(DSA_UNSUPPORTED_SHAPE,
+                "the workspace this shape needs (%zu bytes) exceeds the allocation-free "
+                "scratch (%zu bytes); use dsa_sparse_attn_bwd with a caller workspace",
+                need, dsa::kBwdScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = dsa::bwd_scratch_address(&ws);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_status(e, "dsa_sparse_attn_bwd_noalloc: scratch address");
+  }
+  (void)hipGetLastError();
+  const dsa::AttnArgs a = bwd_args(q, k, v, out, dout, lse, idx, q_pos, Sq, Sk, heads, topk, scale,
+                                   dq, dk, dv, ws);
+  return hip_status(dsa::launch_attn_bwd(a, stream), "dsa_sparse_attn_bwd_noalloc launch");
+}

@@ -148,5 +148,10 @@ inline BwdWorkspace bwd_ws_layout(int64_t Sq, int64_t Sk, int heads, int topk) {
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s);
 
+// Allocation-free backward: the largest workspace its device-resident scratch
+// array holds, and that array's device address on the current device (looked
+// up once per device).
+constexpr size_t kBwdScratchBytes = size_t(96) << 20;
+hipError_t bwd_scratch_address(void** out);
 
 }  // namespace dsa

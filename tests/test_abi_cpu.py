@@ -134,6 +134,23 @@ def test_bwd_validation():
     assert L.dsa_sparse_attn_bwd(*a) == 2 and b"Sq*(topk+1)" in L.dsa_last_error()
 
 
+def test_bwd_noalloc_validation():
+    # the allocation-free backward validates like dsa_sparse_attn_bwd and rejects shapes whose
+    # workspace exceeds its 96 MiB scratch, all before any HIP call
+    L = D.lib()
+    args = [P, P, P, P, P, P, P, None, 64, 64, 4, 128, 4, 8, 0.1, P, P, P, None]
+    a = list(args); a[4] = None
+    assert L.dsa_sparse_attn_bwd_noalloc(*a) == 1 and b"dout is NULL" in L.dsa_last_error()
+    a = list(args); a[10] = 65
+    assert L.dsa_sparse_attn_bwd_noalloc(*a) == 2 and b"heads=65" in L.dsa_last_error()
+    a = list(args); a[8] = 1 << 18; a[9] = 1 << 18; a[13] = 128
+    assert D.sparse_attn_bwd_ws_bytes(1 << 18, 1 << 18, 4, 128) > 96 << 20
+    assert L.dsa_sparse_attn_bwd_noalloc(*a) == 2
+    assert b"exceeds the allocation-free scratch" in L.dsa_last_error()
+    # the largest training workload's backward fits
+    assert D.sparse_attn_bwd_ws_bytes(131072, 131072, 4, 128) <= 96 << 20
+
+
 def test_python_binding_checks_dtypes():
     import torch
     q = torch.zeros(4, 4, 64, dtype=torch.float32)
