@@ -33,6 +33,7 @@ import synthetic as syn  # noqa: E402
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 BF16_PEAK = 2.5e15         # flop/s, dense bf16 MFMA
+FP8_PEAK = 5.0e15          # flop/s, dense fp8 MFMA
 SCALE = 1.0 / np.sqrt(128.0)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
@@ -132,6 +133,14 @@ class Layer:
                           q_pos=self.q_pos, scale=SCALE, ws=self.ws_bwd, dq=self.dq, dk=self.dk,
                           dv=self.dv)
 
+    def index_fp8(self, ev):
+        """The fp8 indexer (dsa_index_topk_fp8) as a separate call, with events around it."""
+        t, wl = self.t, self.wl
+        ev[0].record()
+        D.index_topk(t["q_idx"], t["k_idx"], t["w_idx"], topk=wl.topk, q_chunk=wl.q_chunk,
+                     q_pos=self.q_pos, out=self.idx, ws=self.ws_idx, fp8=True)
+        ev[1].record()
+
     def kernels(self, ev):
         """The same work as separate entry-point calls, one after the other on the current
         stream (the stream every kernel of these calls is launched on), with events around
@@ -187,6 +196,13 @@ def run(layer: Layer, steps: int, warmup: int):
            "fwd": [e[1].elapsed_time(e[2]) / 1e3 for e in kev]}
     if bw:
         per["bwd"] = [e[2].elapsed_time(e[3]) / 1e3 for e in kev]
+    # the fp8 indexer variant, timed the same way (its ids equal the bf16 path's on these inputs)
+    layer.index_fp8([torch.cuda.Event(enable_timing=True) for _ in range(2)])
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for s in range(steps):
+        layer.index_fp8(fev[s])
+    torch.cuda.synchronize()
+    per["index_fp8"] = [e[0].elapsed_time(e[1]) / 1e3 for e in fev]
     avg = {k: float(np.mean(v)) for k, v in per.items()}
     avg_step = {k: float(np.mean(v)) for k, v in step_parts.items()}
     return wall, avg, avg_step
@@ -217,6 +233,12 @@ def training_modes(layer: Layer, steps: int, warmup: int):
         res[mode] = {"ms_per_step": round(ms, 3), "kept_device_bytes": int(kept[0]),
                      "kept_host_bytes": int(kept[1])}
     return res
+
+
+def separate_sum(avg: dict) -> float:
+    """Seconds of one step run as separate calls (the bf16 indexer, forward and backward; the fp8
+    indexer variant is timed beside them, not part of the step)."""
+    return sum(v for k, v in avg.items() if k != "index_fp8")
 
 
 def source_hash(rel: str) -> str:
@@ -325,6 +347,16 @@ def main():
                 "launches": "separate calls after the timed steps"}
     kernels = {n: {"ms": round(v["s"] * 1e3, 3), "achieved": round(v["achieved"], 2), "unit": v["unit"],
                    "frac": round(v["achieved"] / v["peak"], 4)} for n, v in kern.items()}
+    # the indexer beside the dominant kernel (bf16 MFMA-bound), and the fp8 variant (opt-in,
+    # dsa_index_topk_fp8) against the fp8 peak and, for comparison, the bf16 one
+    ki = kern["indexer_topk_kernel"]
+    roofline["indexer"] = {"kernel": "indexer_topk_kernel", "bound": "mfma", "achieved": round(ki["achieved"], 2),
+                           "peak": ki["peak"], "unit": "TFLOP/s", "frac": round(ki["achieved"] / ki["peak"], 4),
+                           "ms_per_launch": round(ki["s"] * 1e3, 3)}
+    f8 = w["index_flop"] / avg["index_fp8"] / 1e12
+    kernels["indexer32_fp8_kernel"] = {"ms": round(avg["index_fp8"] * 1e3, 3), "achieved": round(f8, 2),
+                                       "unit": "TFLOP/s", "frac": round(f8 * 1e12 / FP8_PEAK, 4),
+                                       "frac_of_bf16_peak": round(f8 * 1e12 / BF16_PEAK, 4)}
 
     secondary = None
     if args.secondary and args.secondary != wl.name:
@@ -341,8 +373,9 @@ def main():
                      "pass": "index+fwd+bwd" if sw.backward else "index+fwd",
                      "ms": {k: round(v * 1e3, 3) for k, v in savg.items()},
                      "step_ms": {k: round(v * 1e3, 3) for k, v in sstep.items()},
-                     "separate_calls_ms_per_step": round(sum(savg.values()) * 1e3, 3),
+                     "separate_calls_ms_per_step": round(separate_sum(savg) * 1e3, 3),
                      "index_mfma_frac": round(sws["index_flop"] / savg["index"] / BF16_PEAK, 4),
+                     "index_fp8_mfma_frac": round(sws["index_flop"] / savg["index_fp8"] / FP8_PEAK, 4),
                      "fwd_gather_GBps": round(sws["fwd_bytes"] / savg["fwd"] / 1e9, 1)}
         if sw.backward:
             secondary["bwd_GBps"] = round(sws["bwd_bytes"] / savg["bwd"] / 1e9, 1)
@@ -367,9 +400,12 @@ def main():
                "pass": "index+fwd+bwd" if ow.backward else "index+fwd",
                "ms": {k: round(v * 1e3, 3) for k, v in oavg.items()},
                "index_mfma_frac": round(ows["index_flop"] / oavg["index"] / BF16_PEAK, 4),
+               "index_fp8_mfma_frac": round(ows["index_flop"] / oavg["index_fp8"] / FP8_PEAK, 4),
                # algorithmic bytes per second; K and V of these workloads (8 to 64 MiB) stay in
-               # the caches, so the rate can exceed the HBM peak
-               "fwd_gather_GBps": round(ows["fwd_bytes"] / oavg["fwd"] / 1e9, 1)}
+               # the L2 and the 256 MB MALL, so this is a cache-bandwidth rate, not a fraction
+               # of the HBM roofline (it can exceed the HBM peak)
+               "fwd_gather_GBps": round(ows["fwd_bytes"] / oavg["fwd"] / 1e9, 1),
+               "gather_bound": "cache-resident K/V (no HBM roofline)"}
         if ow.backward:
             rec["bwd_GBps"] = round(ows["bwd_bytes"] / oavg["bwd"] / 1e9, 1)
         others.append(rec)
@@ -402,7 +438,7 @@ def main():
         # the step's parts as timed (indexer and forward pipelined in one call), and the same
         # work as separate calls one after the other (the per-kernel durations above)
         "step_ms": {k: round(v * 1e3, 3) for k, v in avg_step.items()},
-        "separate_calls_ms_per_step": round(sum(avg.values()) * 1e3, 3),
+        "separate_calls_ms_per_step": round(separate_sum(avg) * 1e3, 3),
         "index_mfma_frac": round(w["index_flop"] / avg["index"] / BF16_PEAK, 4),
         "fwd_gather_GBps": round(w["fwd_bytes"] / avg["fwd"] / 1e9, 1),
         "cpu_baseline": cpu,

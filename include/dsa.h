@@ -128,6 +128,31 @@ int dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_idx,
                    int32_t idx_dim, int32_t pool, int32_t topk, int32_t q_chunk,
                    int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Indexer + top-k on fp8 operands (opt-in variant).
+ *
+ * The same selection as dsa_index_topk, with the same arguments, workspace
+ * (dsa_index_topk_ws_bytes) and output, computed on the gfx950 fp8 matrix
+ * cores: the pooled keys and the folded queries bf16(w * q) are rounded to
+ * OCP e4m3 (fp8) instead of bf16, and one v_mfma_f32_32x32x64_f8f6f4 scores 8
+ * queries x 4 heads against 32 pools over the whole 64-dim contraction (half
+ * the matrix-core time and half the key bytes of the bf16 path per pair).
+ * Dot products accumulate in fp32.  The precision theme of the pages (SkyRL
+ * news item, section "4. 去掉多余 fp32") is the motivation; the reading is
+ * that the selection may be computed on e4m3 operands.  For integer indexer
+ * inputs in [-3, 3] every operand is exact in e4m3 (w * q is an integer in
+ * [-9, 9], a pooled key a multiple of 1/4 in [-3, 3]), so the ids equal the
+ * exact ranking and dsa_index_topk's ids bit for bit; other inputs carry the
+ * e4m3 rounding (3 mantissa bits; magnitudes above 448 saturate) and may rank
+ * differently.
+ *
+ * Supported: as dsa_index_topk, with 1 <= idx_heads <= 4.
+ */
+int dsa_index_topk_fp8(const void* q_idx, const void* k_idx, const void* w_idx,
+                       const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t idx_heads,
+                       int32_t idx_dim, int32_t pool, int32_t topk, int32_t q_chunk,
+                       int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Tuning override of the indexer's workgroup sub-tile, process-wide: 4, 8 or
  * 16 queries per wave (16-, 32- or 64-query sub-tiles) for every later
  * indexer launch, or 0 to let each call choose by its query count (the

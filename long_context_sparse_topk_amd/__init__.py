@@ -40,6 +40,8 @@ SIGNATURES = {
     "dsa_index_topk_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32, _I32]),
     "dsa_index_topk": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32,
                                       _P, _P, _SZ, _P]),
+    "dsa_index_topk_fp8": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32,
+                                          _P, _P, _SZ, _P]),
     "dsa_set_index_queries_per_wave": (ctypes.c_int, [_I32]),
     "dsa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
                                            _F, _P, _P, _P]),
@@ -155,8 +157,11 @@ def sparse_attn_bwd_ws_bytes(Sq: int, Sk: int, heads: int, topk: int) -> int:
 
 
 def index_topk(q_idx, k_idx, w_idx, *, topk: int, q_chunk: int = 256, q_pos=None,
-               out=None, ws=None) -> torch.Tensor:
-    """Top-k pool ids [Sq, topk] int32, ascending, -1 padded."""
+               out=None, ws=None, fp8: bool = False) -> torch.Tensor:
+    """Top-k pool ids [Sq, topk] int32, ascending, -1 padded.
+
+    fp8=True calls dsa_index_topk_fp8: the same selection on e4m3 operands (exact, and
+    equal to the bf16 path, for integer indexer inputs in [-3, 3])."""
     L = lib()
     dev = q_idx.device
     _want(q_idx, "q_idx", torch.bfloat16, 3, dev)
@@ -176,10 +181,10 @@ def index_topk(q_idx, k_idx, w_idx, *, topk: int, q_chunk: int = 256, q_pos=None
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     else:
         _want(ws, "ws", torch.uint8, 1, dev)
-    st = L.dsa_index_topk(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q_pos), Sq, Sk, HI, DI, POOL,
-                          topk, q_chunk, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                          _stream(dev))
-    _check("dsa_index_topk", st)
+    fn = L.dsa_index_topk_fp8 if fp8 else L.dsa_index_topk
+    st = fn(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q_pos), Sq, Sk, HI, DI, POOL, topk, q_chunk,
+            _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check("dsa_index_topk_fp8" if fp8 else "dsa_index_topk", st)
     return out
 
 

@@ -195,6 +195,38 @@ DSA_EXPORT int dsa_index_topk(const void* q_idx, const void* k_idx, const void* 
   return hip_status(dsa::launch_index_topk(a, stream), "dsa_index_topk launch");
 }
 
+DSA_EXPORT int dsa_index_topk_fp8(const void* q_idx, const void* k_idx, const void* w_idx,
+                                  const int32_t* q_pos, int64_t Sq, int64_t Sk, int32_t idx_heads,
+                                  int32_t idx_dim, int32_t pool, int32_t topk, int32_t q_chunk,
+                                  int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  int st;
+  if ((st = check_ptr(q_idx, "q_idx", 16))) return st;
+  if ((st = check_ptr(k_idx, "k_idx", 16))) return st;
+  if ((st = check_ptr(w_idx, "w_idx", 2))) return st;
+  if ((st = check_ptr(idx_out, "idx_out", 4))) return st;
+  if ((st = check_ptr(ws, "ws", 256))) return st;
+  if ((st = check_index_shape(Sq, Sk, idx_heads, idx_dim, pool, topk, q_chunk, q_pos, ws_bytes)))
+    return st;
+  if (idx_heads > 4)
+    return fail(DSA_UNSUPPORTED_SHAPE, "idx_heads=%d (the fp8 indexer supports 1..4)", idx_heads);
+
+  (void)hipGetLastError();
+  dsa::IndexArgs a{};
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.k_idx = static_cast<const uint16_t*>(k_idx);
+  a.w_idx = static_cast<const uint16_t*>(w_idx);
+  a.q_pos = q_pos;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.heads = idx_heads;
+  a.topk = topk;
+  a.q_chunk = q_chunk;
+  a.idx_out = idx_out;
+  a.ws = ws;
+  return hip_status(dsa::launch_index_topk_fp8(a, stream), "dsa_index_topk_fp8 launch");
+}
+
 DSA_EXPORT int dsa_set_index_queries_per_wave(int32_t queries_per_wave) {
   g_err[0] = '\0';
   if (!dsa::set_index_queries_per_wave(queries_per_wave))

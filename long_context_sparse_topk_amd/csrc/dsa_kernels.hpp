@@ -77,6 +77,8 @@ struct IndexArgs {
 };
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
+// The same selection on fp8 (e4m3) operands, 32x32x64 MFMA; same workspace layout.
+hipError_t launch_index_topk_fp8(const IndexArgs& a, hipStream_t s);
 
 // Process-wide override of the indexer's workgroup sub-tile (queries per wave 4, 8 or 16;
 // 0 = chosen per call).  Returns false for other values.

@@ -91,6 +91,17 @@ def test_index_validation(kw, status, msg):
     assert msg in D.lib().dsa_last_error().decode()
 
 
+def test_index_fp8_validation():
+    # the fp8 indexer validates like dsa_index_topk and takes 1..4 indexer heads
+    L = D.lib()
+    args = [P, P, P, None, 64, 64, 5, 64, 4, 8, 256, P, P, 1 << 40, None]
+    assert L.dsa_index_topk_fp8(*args) == 2 and b"fp8 indexer supports 1..4" in L.dsa_last_error()
+    a = list(args); a[6] = 4; a[7] = 32
+    assert L.dsa_index_topk_fp8(*a) == 2 and b"idx_dim=32" in L.dsa_last_error()
+    a = list(args); a[6] = 4; a[13] = 100
+    assert L.dsa_index_topk_fp8(*a) == 3
+
+
 def _fwd(**kw):
     a = dict(q=P, k=P, v=P, idx=P, q_pos=None, Sq=64, Sk=64, H=4, D=128, pool=4, topk=8,
              scale=0.1, out=P, lse=P)

@@ -27,14 +27,20 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=[4, 8, 16])
-def queries_per_wave(request):
-    """Run an indexer test with each workgroup sub-tile (16, 32 and 64 queries).
+_INDEX_FP8 = [False]   # the variant gpu_index() calls: dsa_index_topk or dsa_index_topk_fp8
 
-    The library picks one by query count and launch; dsa_set_index_queries_per_wave forces it."""
-    D.set_index_queries_per_wave(request.param)
+
+@pytest.fixture(params=[4, 8, 16, "fp8"])
+def queries_per_wave(request):
+    """Run an indexer test with each workgroup sub-tile of the bf16 indexer (16, 32 and 64
+    queries; dsa_set_index_queries_per_wave forces one) and with the fp8 indexer
+    (dsa_index_topk_fp8), which must give the same ids on these integer inputs."""
+    fp8 = request.param == "fp8"
+    D.set_index_queries_per_wave(0 if fp8 else request.param)
+    _INDEX_FP8[0] = fp8
     yield request.param
     D.set_index_queries_per_wave(0)
+    _INDEX_FP8[0] = False
 
 
 def _bits(x):
@@ -48,10 +54,10 @@ def _int_inputs(Sq, Sk, seed, heads=4):
             _bits(rng.integers(-3, 4, size=(Sq, heads))))
 
 
-def gpu_index(q_idx, k_idx, w_idx, topk, q_chunk=256, q_pos=None):
+def gpu_index(q_idx, k_idx, w_idx, topk, q_chunk=256, q_pos=None, fp8=None):
     qp = None if q_pos is None else dev_i32(q_pos)
     idx = D.index_topk(dev_bf16(q_idx), dev_bf16(k_idx), dev_bf16(w_idx), topk=topk,
-                       q_chunk=q_chunk, q_pos=qp)
+                       q_chunk=q_chunk, q_pos=qp, fp8=_INDEX_FP8[0] if fp8 is None else fp8)
     torch.cuda.synchronize()
     return idx.cpu().numpy()
 
@@ -381,6 +387,12 @@ def test_full_size_pipeline(name):
     ref_idx = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], qp, wl.topk, rows=rows)
     got_idx = idx[torch.from_numpy(rows).cuda()].cpu().numpy()
     assert_idx_equal(f"{name} idx", got_idx, ref_idx, rows)
+    # the fp8 indexer on the same integer inputs: the same ids (exact in e4m3)
+    idx8 = D.index_topk(dev["q_idx"], dev["k_idx"], dev["w_idx"], topk=wl.topk, q_chunk=wl.q_chunk,
+                        q_pos=tq, fp8=True)
+    torch.cuda.synchronize()
+    assert_idx_equal(f"{name} idx fp8", idx8[torch.from_numpy(rows).cuda()].cpu().numpy(), ref_idx, rows)
+    del idx8
     # attention rows: the oracle uses its own selection for those rows
     full_idx = np.zeros((wl.sq, wl.topk), np.int32)
     full_idx[rows] = ref_idx
