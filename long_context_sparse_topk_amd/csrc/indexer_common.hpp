@@ -32,7 +32,7 @@ constexpr int kExactSharedSlots = 64;      // exact-pass grid when the CUs are s
 // found by a radix select over the bits where the keys differ (their OR xor
 // AND), 8 bits per pass, with a per-wave LDS histogram.
 
-constexpr int kR = 24;
+constexpr int kR = 8;
 constexpr int kChunk = kWave * kR;
 
 __device__ __forceinline__ void load_chunk(const u32x2_t* __restrict__ list, int base, int n,

@@ -645,13 +645,19 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
 }
 
 // The kernels are plain functions around the templated body (in the host pass a
-// kernel template of this size lost its host stub).  fp8, two row blocks of 8
-// queries a wave (64 queries a workgroup), two workgroups a CU.
-__global__ __launch_bounds__(kThreads, 2) void indexer32_fp8_kernel(KernelArgs a) {
-  indexer32_body<true, 2, true>(a);
+// kernel template of this size lost its host stub).  fp8: one row block of 8
+// queries a wave (32 queries a workgroup), held to 128 registers so that four
+// workgroups share a CU (four waves a SIMD; 32 KB of LDS each).  Measured at
+// S = 2^20 (same ids): 62.7 ms, against 76.1 ms at three waves a SIMD, 91.9 ms
+// with 16 queries a wave at two waves a SIMD, and 105.5 ms with 8 queries a
+// wave at two.  Each extra wave a SIMD hides more of the others' dependency
+// chains (MFMA results before the epilogue, ballots before branches).
+constexpr int kNRB32 = 1;
+__global__ __launch_bounds__(kThreads, 4) void indexer32_fp8_kernel(KernelArgs a) {
+  indexer32_body<true, kNRB32, true>(a);
 }
-__global__ __launch_bounds__(kThreads, 2) void indexer32_fp8_exact_kernel(KernelArgs a) {
-  indexer32_body<false, 2, true>(a);
+__global__ __launch_bounds__(kThreads, 4) void indexer32_fp8_exact_kernel(KernelArgs a) {
+  indexer32_body<false, kNRB32, true>(a);
 }
 
 // Workgroups the device keeps resident at once, and its CU count (cached per device).
@@ -677,7 +683,7 @@ Residency index32_residency() {
 }
 
 void launch32_passes(KernelArgs a, const IndexArgs& ia, uint32_t* fb_count, hipStream_t s) {
-  constexpr int64_t qtile = (int64_t)kWaves * 8 * 2;   // the kernels' 64-query tile
+  constexpr int64_t qtile = (int64_t)kWaves * 8 * kNRB32;   // the kernels' query tile
   const int64_t lists = index_slots(ia.Sq) * kIndexQueryTile;
   int64_t slots = (ia.Sq + qtile - 1) / qtile;
   if (slots > lists / qtile) slots = lists / qtile;
