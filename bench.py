@@ -133,6 +133,13 @@ class Layer:
                           q_pos=self.q_pos, scale=SCALE, ws=self.ws_bwd, dq=self.dq, dk=self.dk,
                           dv=self.dv)
 
+    def step_fp8(self):
+        """The pipelined call with the fp8 indexer (dsa_index_attn_fwd_fp8)."""
+        t, wl = self.t, self.wl
+        D.index_attn_fwd(t["q_idx"], t["k_idx"], t["w_idx"], t["q"], t["k"], t["v"], topk=wl.topk,
+                         q_chunk=wl.q_chunk, q_pos=self.q_pos, scale=SCALE, idx=self.idx, out=self.out,
+                         lse=self.lse, ws=self.ws_idx, fp8=True)
+
     def index_fp8(self, ev):
         """The fp8 indexer (dsa_index_topk_fp8) as a separate call, with events around it."""
         t, wl = self.t, self.wl
@@ -196,6 +203,17 @@ def run(layer: Layer, steps: int, warmup: int):
            "fwd": [e[1].elapsed_time(e[2]) / 1e3 for e in kev]}
     if bw:
         per["bwd"] = [e[2].elapsed_time(e[3]) / 1e3 for e in kev]
+    # the step's pipelined call with the fp8 indexer instead (same ids on these inputs)
+    layer.step_fp8()
+    ev8 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ts8 = []
+    for _ in range(steps):
+        ev8[0].record()
+        layer.step_fp8()
+        ev8[1].record()
+        torch.cuda.synchronize()
+        ts8.append(ev8[0].elapsed_time(ev8[1]) / 1e3)
+    step_parts["index_fwd_pipelined_fp8_indexer"] = ts8
     # the fp8 indexer variant, timed the same way (its ids equal the bf16 path's on these inputs)
     layer.index_fp8([torch.cuda.Event(enable_timing=True) for _ in range(2)])
     fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
@@ -441,6 +459,12 @@ def main():
         "separate_calls_ms_per_step": round(separate_sum(avg) * 1e3, 3),
         "index_mfma_frac": round(w["index_flop"] / avg["index"] / BF16_PEAK, 4),
         "fwd_gather_GBps": round(w["fwd_bytes"] / avg["fwd"] / 1e9, 1),
+        # the same step with the fp8 indexer (dsa_index_attn_fwd_fp8; its ids equal the bf16
+        # indexer's on these integer inputs), timed with events around each call
+        "fp8_indexer_step": {"ms_per_step": round((avg_step["index_fwd_pipelined_fp8_indexer"]
+                                                   + avg_step.get("bwd", 0.0)) * 1e3, 3),
+                             "tokens_per_s": round(wl.sq / (avg_step["index_fwd_pipelined_fp8_indexer"]
+                                                            + avg_step.get("bwd", 0.0)), 1)},
         "cpu_baseline": cpu,
         "secondary": secondary,
         "others": others,

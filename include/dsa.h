@@ -227,6 +227,17 @@ int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx, 
                        float scale, int32_t* idx_out, void* out, float* lse, void* ws,
                        size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream);
 
+/* The same pipelined call with the fp8 indexer (dsa_index_topk_fp8) in place of
+ * the bf16 one: the same arguments, workspace and streams; idx_out, out and lse
+ * equal those of dsa_index_topk_fp8 followed by dsa_sparse_attn_fwd bit for
+ * bit.  Supported: as dsa_index_attn_fwd, with 1 <= idx_heads <= 4. */
+int dsa_index_attn_fwd_fp8(const void* q_idx, const void* k_idx, const void* w_idx, const void* q,
+                           const void* k, const void* v, const int32_t* q_pos, int64_t Sq,
+                           int64_t Sk, int32_t idx_heads, int32_t idx_dim, int32_t heads,
+                           int32_t head_dim, int32_t pool, int32_t topk, int32_t q_chunk,
+                           float scale, int32_t* idx_out, void* out, float* lse, void* ws,
+                           size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream);
+
 /* ---------------------------------------------------------------------------
  * Sparse attention backward.
  *

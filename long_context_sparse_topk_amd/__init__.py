@@ -48,6 +48,8 @@ SIGNATURES = {
     "dsa_index_attn_fwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32, _I32]),
     "dsa_index_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32,
                                           _I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _SZ, _P, _P]),
+    "dsa_index_attn_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32,
+                                              _I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _SZ, _P, _P]),
     "dsa_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
     "dsa_sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32,
                                            _I32, _I32, _F, _P, _P, _P, _P, _SZ, _P]),
@@ -231,11 +233,12 @@ def _aux_stream(dev):
 
 def index_attn_fwd(q_idx, k_idx, w_idx, q, k, v, *, topk: int, q_chunk: int = 256, q_pos=None,
                    scale: float | None = None, idx=None, out=None, lse=None, ws=None,
-                   aux_stream=None):
+                   aux_stream=None, fp8: bool = False):
     """index_topk then sparse_attn_fwd, pipelined over query chunks on two streams.
 
     Returns (idx [Sq, topk] int32, out [Sq, H, 128] bf16, lse [Sq, H] fp32), equal bit for
     bit to the two separate calls.  The current stream waits for all of the work on return.
+    fp8=True uses the fp8 indexer (dsa_index_attn_fwd_fp8).
     """
     L = lib()
     dev = q_idx.device
@@ -265,12 +268,11 @@ def index_attn_fwd(q_idx, k_idx, w_idx, q, k, v, *, topk: int, q_chunk: int = 25
     else:
         _want(ws, "ws", torch.uint8, 1, dev)
     aux = _aux_stream(dev) if aux_stream is None else aux_stream
-    st = L.dsa_index_attn_fwd(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(v),
-                              _ptr(q_pos), Sq, Sk, HI, DI, H, D, POOL, topk, q_chunk, scale,
-                              _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream(dev),
-                              ctypes.c_void_p(aux.cuda_stream))
-    _check("dsa_index_attn_fwd", st)
+    fn = L.dsa_index_attn_fwd_fp8 if fp8 else L.dsa_index_attn_fwd
+    st = fn(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(v), _ptr(q_pos), Sq, Sk, HI,
+            DI, H, D, POOL, topk, q_chunk, scale, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(dev), ctypes.c_void_p(aux.cuda_stream))
+    _check("dsa_index_attn_fwd_fp8" if fp8 else "dsa_index_attn_fwd", st)
     return idx, out, lse
 
 

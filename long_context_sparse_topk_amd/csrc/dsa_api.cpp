@@ -279,13 +279,19 @@ DSA_EXPORT size_t dsa_index_attn_fwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t id
   return dsa_index_topk_ws_bytes(Sq, Sk, idx_heads, idx_dim, pool, topk, q_chunk);
 }
 
-DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx,
-                                  const void* q, const void* k, const void* v,
-                                  const int32_t* q_pos, int64_t Sq, int64_t Sk,
-                                  int32_t idx_heads, int32_t idx_dim, int32_t heads,
-                                  int32_t head_dim, int32_t pool, int32_t topk, int32_t q_chunk,
-                                  float scale, int32_t* idx_out, void* out, float* lse, void* ws,
-                                  size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream) {
+namespace {
+
+// The pipelined call with the bf16 or the fp8 indexer.  Indexer chunks after the
+// first share the CUs with the forward: the bf16 indexer keeps one workgroup a
+// CU there (its 64-query sub-tile), the fp8 one two (its 32-query workgroups
+// hold 128 registers a wave; measured at S = 2^20: 190 ms with two, 260 with
+// one, 214 with three).
+int index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx, const void* q,
+                   const void* k, const void* v, const int32_t* q_pos, int64_t Sq, int64_t Sk,
+                   int32_t idx_heads, int32_t idx_dim, int32_t heads, int32_t head_dim,
+                   int32_t pool, int32_t topk, int32_t q_chunk, float scale, int32_t* idx_out,
+                   void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                   hipStream_t aux_stream, bool fp8) {
   g_err[0] = '\0';
   int st;
   if ((st = check_ptr(q_idx, "q_idx", 16))) return st;
@@ -301,6 +307,8 @@ DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const vo
   if ((st = check_index_shape(Sq, Sk, idx_heads, idx_dim, pool, topk, q_chunk, q_pos, ws_bytes)))
     return st;
   if ((st = check_attn_shape(Sq, Sk, heads, head_dim, pool, topk, scale, q_pos))) return st;
+  if (fp8 && idx_heads > 4)
+    return fail(DSA_UNSUPPORTED_SHAPE, "idx_heads=%d (the fp8 indexer supports 1..4)", idx_heads);
 
   const int n = aux_stream == stream ? 1 : pipe_chunks(Sq);
   // events: one per chunk (indexer done) and one for the forward stream's end
@@ -340,9 +348,9 @@ DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const vo
     ia.q_chunk = q_chunk;
     ia.idx_out = idx_out + r0 * topk;
     ia.ws = ws;
-    ia.max_per_cu = pooled ? 1 : 0;   // the first chunk has the GPU to itself
+    ia.max_per_cu = pooled ? (fp8 ? 2 : 1) : 0;   // the first chunk has the GPU to itself
     ia.pooled = pooled;
-    note(dsa::launch_index_topk(ia, stream));
+    note(fp8 ? dsa::launch_index_topk_fp8(ia, stream) : dsa::launch_index_topk(ia, stream));
     pooled = true;
     hipStream_t fs = stream;
     if (n > 1) {
@@ -372,7 +380,34 @@ DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const vo
     note(hipEventRecord(ev[n], aux_stream));
     note(hipStreamWaitEvent(stream, ev[n], 0));
   }
-  return hip_status(err, "dsa_index_attn_fwd launch");
+  return hip_status(err, fp8 ? "dsa_index_attn_fwd_fp8 launch" : "dsa_index_attn_fwd launch");
+}
+
+}  // namespace
+
+DSA_EXPORT int dsa_index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx,
+                                  const void* q, const void* k, const void* v,
+                                  const int32_t* q_pos, int64_t Sq, int64_t Sk,
+                                  int32_t idx_heads, int32_t idx_dim, int32_t heads,
+                                  int32_t head_dim, int32_t pool, int32_t topk, int32_t q_chunk,
+                                  float scale, int32_t* idx_out, void* out, float* lse, void* ws,
+                                  size_t ws_bytes, hipStream_t stream, hipStream_t aux_stream) {
+  return index_attn_fwd(q_idx, k_idx, w_idx, q, k, v, q_pos, Sq, Sk, idx_heads, idx_dim, heads,
+                        head_dim, pool, topk, q_chunk, scale, idx_out, out, lse, ws, ws_bytes,
+                        stream, aux_stream, false);
+}
+
+DSA_EXPORT int dsa_index_attn_fwd_fp8(const void* q_idx, const void* k_idx, const void* w_idx,
+                                      const void* q, const void* k, const void* v,
+                                      const int32_t* q_pos, int64_t Sq, int64_t Sk,
+                                      int32_t idx_heads, int32_t idx_dim, int32_t heads,
+                                      int32_t head_dim, int32_t pool, int32_t topk,
+                                      int32_t q_chunk, float scale, int32_t* idx_out, void* out,
+                                      float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                                      hipStream_t aux_stream) {
+  return index_attn_fwd(q_idx, k_idx, w_idx, q, k, v, q_pos, Sq, Sk, idx_heads, idx_dim, heads,
+                        head_dim, pool, topk, q_chunk, scale, idx_out, out, lse, ws, ws_bytes,
+                        stream, aux_stream, true);
 }
 
 DSA_EXPORT size_t dsa_sparse_attn_bwd_ws_bytes(int64_t Sq, int64_t Sk, int32_t heads,

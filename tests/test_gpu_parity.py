@@ -499,6 +499,7 @@ def test_full_size_backward_sampled_keys(name):
 # pipelined indexer + forward: equal, bit for bit, to the two separate calls
 
 
+@pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("Sq,Sk,H,topk,zigzag,same_stream", [
     (300_001, 300_001, 3, 32, False, False),     # 2 chunks, ragged tail tile
     (262_144, 1 << 20, 2, 16, True, False),      # zig-zag share: q_pos given, 2 chunks
@@ -506,7 +507,7 @@ def test_full_size_backward_sampled_keys(name):
     (32_768 * 8, 32_768 * 8, 2, 16, False, False),  # 2 chunks: 32- then 64-query indexer sub-tiles
     (300_001, 300_001, 3, 32, False, True),      # aux stream == stream: sequential
 ])
-def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream):
+def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream, fp8):
     rng = np.random.default_rng([Sq, H, topk])
     qi, ki, wi = _int_inputs(Sq, Sk, seed=Sq + topk)
     q = _bits(rng.standard_normal((Sq, H, 128)).astype(np.float32))
@@ -515,11 +516,12 @@ def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream):
     pos = syn.zigzag_positions(Sk, 2, 1)[:Sq] if zigzag else None
     tq = None if pos is None else dev_i32(pos)
     dqi, dki, dwi, dq, dk, dv = (dev_bf16(x) for x in (qi, ki, wi, q, k, v))
-    note(f"pipelined Sq={Sq} Sk={Sk} H={H} topk={topk} zigzag={zigzag} same_stream={same_stream}")
+    note(f"pipelined Sq={Sq} Sk={Sk} H={H} topk={topk} zigzag={zigzag} same_stream={same_stream} "
+         f"fp8={fp8}")
     aux = torch.cuda.current_stream() if same_stream else None
     idx_p, out_p, lse_p = D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, q_pos=tq,
-                                           scale=SCALE, aux_stream=aux)
-    idx_s = D.index_topk(dqi, dki, dwi, topk=topk, q_pos=tq)
+                                           scale=SCALE, aux_stream=aux, fp8=fp8)
+    idx_s = D.index_topk(dqi, dki, dwi, topk=topk, q_pos=tq, fp8=fp8)
     out_s, lse_s = D.sparse_attn_fwd(dq, dk, dv, idx_s, q_pos=tq, scale=SCALE)
     torch.cuda.synchronize()
     assert torch.equal(idx_p, idx_s), "pipelined idx differs from dsa_index_topk"
@@ -540,7 +542,8 @@ def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream):
                  rel=1e-4, allowance=False)
 
 
-def test_pipelined_exact_fallback():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_pipelined_exact_fallback(fp8):
     # the threshold trap at two chunks: nearly every row fails both sampled thresholds, so the
     # exact pass (a small grid while the forward shares the CUs) scores them
     S, topk, H = 262_144 + 100, 64, 1
@@ -551,10 +554,10 @@ def test_pipelined_exact_fallback():
     q = _bits(rng.standard_normal((S, H, 128)).astype(np.float32))
     k = _bits(rng.standard_normal((S, 128)).astype(np.float32))
     v = _bits(rng.standard_normal((S, 128)).astype(np.float32))
-    note("pipelined threshold trap, 2 chunks")
+    note(f"pipelined threshold trap, 2 chunks, fp8={fp8}")
     dqi, dki, dwi, dq, dk, dv = (dev_bf16(x) for x in (qi, k_idx, wi, q, k, v))
-    idx_p, out_p, lse_p = D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, scale=SCALE)
-    idx_s = D.index_topk(dqi, dki, dwi, topk=topk)
+    idx_p, out_p, lse_p = D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, scale=SCALE, fp8=fp8)
+    idx_s = D.index_topk(dqi, dki, dwi, topk=topk, fp8=fp8)
     out_s, lse_s = D.sparse_attn_fwd(dq, dk, dv, idx_s, scale=SCALE)
     torch.cuda.synchronize()
     assert torch.equal(idx_p, idx_s) and torch.equal(out_p, out_s) and torch.equal(lse_p, lse_s)
