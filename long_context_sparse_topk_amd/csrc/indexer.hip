@@ -222,6 +222,7 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) tp = max(tp, lds_np[w]);
     const int ntp = (tp + kPT - 1) / kPT;   // pool tiles in the tile's causal range
+    const int stride = sample_stride(ntp, topk);
 
     float tau[kRB], tau2[kRB];  // running thresholds, and the retry's
 #pragma unroll
@@ -334,8 +335,8 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
         // r from the fraction f of the query's causal pools the sample
         // covers; 0 = no estimate (threshold stays -inf)
         const int n_full = nc[rb] / kPT, part = nc[rb] % kPT;
-        const int s_q = kPT * ((n_full + kSampleStride - 1) / kSampleStride) +
-                        (n_full % kSampleStride == 0 ? part : 0);
+        const int s_q = kPT * ((n_full + stride - 1) / stride) +
+                        (n_full % stride == 0 ? part : 0);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const float z = m == 0 ? kSampleZ1 : kSampleZ2;
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
       // merged into the 8 kept ones by taking the larger of kept[4+j] and
       // new[3-j] (the top 8 of the union, in bitonic order), and the 8 are
       // sorted again by a bitonic half-cleaner network (3 x 4 exchanges).
-      stream(0, kSampleStride, [](int) {}, [&](float (&sc)[kRB][4], int) {
+      stream(0, stride, [](int) {}, [&](float (&sc)[kRB][4], int) {
         auto cx = [](float& hi, float& lo) {
           const float h = fmaxf(hi, lo);
           lo = fminf(hi, lo);

@@ -291,6 +291,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) tp = max(tp, lds_np[w]);
     const int ntp = (tp + kPT - 1) / kPT;   // pool tiles in the tile's causal range
+    const int stride = sample_stride(ntp, topk);
 
     float tau[kNRB][4], tau2[kNRB][4];  // running thresholds, and the retry's
 #pragma unroll
@@ -330,14 +331,22 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         buf = buf == kRing - 1 ? 0 : buf + 1;
         lbuf = lbuf == kRing - 1 ? 0 : lbuf + 1;
 
+        // both column blocks' operands read and both products issued before the
+        // first epilogue, which then runs while the second product is in flight
         float sc[kNRB][2][4];
+        Op Bc[2];
+        read_b<kFp8>(kb, c, h, Bc[0]);
+        read_b<kFp8>(kb, 32 + c, h, Bc[1]);
+        f32x16_t xs[kNRB][2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int rb = 0; rb < kNRB; ++rb) xs[rb][cb] = mma32<kFp8>(A[rb], Bc[cb]);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-          Op B;
-          read_b<kFp8>(kb, 32 * cb + c, h, B);
 #pragma unroll
           for (int rb = 0; rb < kNRB; ++rb) {
-            const f32x16_t x = mma32<kFp8>(A[rb], B);
+            const f32x16_t x = xs[rb][cb];
             // epilogue: clamp each head to the side of its weight, sum the heads
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -376,8 +385,8 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         for (int i = 0; i < 4; ++i) {
           const int n = nc[rb][i];
           const int n_full = n / kPT, part = n % kPT;
-          const int s_q = kPT * ((n_full + kSampleStride - 1) / kSampleStride) +
-                          (n_full % kSampleStride == 0 ? part : 0);
+          const int s_q = kPT * ((n_full + stride - 1) / stride) +
+                          (n_full % stride == 0 ? part : 0);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const float z = m == 0 ? kSampleZ1 : kSampleZ2;
@@ -401,7 +410,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
       // per tile and query the lane's 2 new scores are sorted, merged into the 4
       // kept ones by taking the larger of kept[2+j] and new[1-j] (the top 4 of
       // the union, in bitonic order), and the 4 sorted by a half-cleaner network
-      stream(0, kSampleStride, [](int) {}, [&](float (&sc)[kNRB][2][4], int) {
+      stream(0, stride, [](int) {}, [&](float (&sc)[kNRB][2][4], int) {
         auto cx = [](float& hi, float& lo) {
           const float t = fmaxf(hi, lo);
           lo = fminf(hi, lo);

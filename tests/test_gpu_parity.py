@@ -155,18 +155,20 @@ def _threshold_trap_keys(S, unsampled):
     """Indexer keys for q = w = 1, where the score of pool p is 4 * T(p).
 
     The indexer estimates each query's threshold from a sample of every 16th
-    tile of 64 pools (tiles 0, 16, 32, ...).  Here tile 0 holds the best
-    scores, T = 150 - p, the other sampled tiles T = 50, and every pool
-    outside the sample T = `unsampled`, so the sample overstates how good the
-    unsampled pools are.  With `unsampled` = 125 the small-margin threshold of
-    long queries (about the 18th best sampled score) keeps fewer than k pools
-    and the larger-margin retry (about the 34th) keeps every unsampled pool;
-    with 10 both keep fewer than k and those rows need the exact pass.
+    tile of 64 pools (tiles 0, 16, 32, ...), or of every 8th for query tiles
+    whose causal range spans at most 128 pool tiles when k <= 256 (as here).
+    Tile 0 holds the best scores, T = 150 - p, the other tiles of either sample
+    (every 8th) T = 50, and every pool outside them T = `unsampled`, so the
+    sample overstates how good the unsampled pools are.  With `unsampled` = 125
+    the small-margin threshold of long queries (about the 23rd best sampled
+    score at S = 10240, k = 64) keeps fewer than k pools and the larger-margin
+    retry (about the 40th) keeps every unsampled pool; with 10 both keep fewer
+    than k and those rows need the exact pass.
     """
     n = S // 4
     T = np.full(n, unsampled)
     tile = np.arange(n) // 64
-    T[tile % 16 == 0] = 50
+    T[tile % 8 == 0] = 50
     T[:64] = 150 - np.arange(64)
     kp = np.clip(T[:, None] - 3 * np.arange(64)[None, :], 0, 3)   # row sums = T
     return _bits(np.repeat(kp, 4, axis=0).astype(np.float32))
