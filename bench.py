@@ -36,10 +36,12 @@ BF16_PEAK = 2.5e15         # flop/s, dense bf16 MFMA
 FP8_PEAK = 5.0e15          # flop/s, dense fp8 MFMA
 SCALE = 1.0 / np.sqrt(128.0)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+_CSRC = "long_context_sparse_topk_amd/csrc/"
 KERNEL_SOURCES = {
-    "attn_fwd_kernel": "long_context_sparse_topk_amd/csrc/attn_fwd.hip",
-    "indexer_topk_kernel": "long_context_sparse_topk_amd/csrc/indexer.hip",
-    "sparse_attn_bwd": "long_context_sparse_topk_amd/csrc/attn_bwd.hip",   # dq + inverse lists + dk/dv
+    "attn_fwd_kernel": [_CSRC + "attn_fwd.hip"],
+    "indexer_topk_kernel": [_CSRC + "indexer.hip", _CSRC + "indexer_common.hpp"],
+    "indexer32_fp8_kernel": [_CSRC + "indexer_mfma32.hip", _CSRC + "indexer_common.hpp"],
+    "sparse_attn_bwd": [_CSRC + "attn_bwd.hip"],   # dq + inverse lists + dk/dv
 }
 
 
@@ -259,10 +261,9 @@ def separate_sum(avg: dict) -> float:
     return sum(v for k, v in avg.items() if k != "index_fp8")
 
 
-def source_hash(rel: str) -> str:
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in (rel, "long_context_sparse_topk_amd/csrc/dsa_device.hpp",
-              "long_context_sparse_topk_amd/csrc/dsa_kernels.hpp"):
+    for f in list(files) + [_CSRC + "dsa_device.hpp", _CSRC + "dsa_kernels.hpp"]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -370,11 +371,13 @@ def main():
     ki = kern["indexer_topk_kernel"]
     roofline["indexer"] = {"kernel": "indexer_topk_kernel", "bound": "mfma", "achieved": round(ki["achieved"], 2),
                            "peak": ki["peak"], "unit": "TFLOP/s", "frac": round(ki["achieved"] / ki["peak"], 4),
+                           "traffic": measured_traffic("indexer_topk_kernel", wl.name),
                            "ms_per_launch": round(ki["s"] * 1e3, 3)}
     f8 = w["index_flop"] / avg["index_fp8"] / 1e12
     kernels["indexer32_fp8_kernel"] = {"ms": round(avg["index_fp8"] * 1e3, 3), "achieved": round(f8, 2),
                                        "unit": "TFLOP/s", "frac": round(f8 * 1e12 / FP8_PEAK, 4),
-                                       "frac_of_bf16_peak": round(f8 * 1e12 / BF16_PEAK, 4)}
+                                       "frac_of_bf16_peak": round(f8 * 1e12 / BF16_PEAK, 4),
+                                       "traffic": measured_traffic("indexer32_fp8_kernel", wl.name)}
 
     secondary = None
     if args.secondary and args.secondary != wl.name:
