@@ -123,6 +123,12 @@ __device__ __forceinline__ bf16x8_t fold_weight(u32x4_t q, float w) {
 template <bool kTwoPhase, int kRB, int kHG>
 __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kernel(KernelArgs a) {
   constexpr int kQW = 4 * kRB;        // queries per wave (kRB row blocks of 4)
+  // list entries per lane the selection holds in registers: the 64-query
+  // sub-tile runs one wave a SIMD beside the forward, where a selection's
+  // list re-reads are exposed (S = 2^20 pipelined: 197.1 ms with 24, 202.0
+  // with 8); the others keep 8 and fit their registers without spilling
+  // (S = 2^17: 2.20 ms against 2.34 with 24)
+  constexpr int kSelectRegs = kRB == 4 ? 24 : 8;
   constexpr int kQTile = kWaves * kQW;  // queries per workgroup tile
   __shared__ __align__(16) u32x4_t lds_k[kRing][kPT * 8];   // ring of (64 pools x 128 B), swizzled
   __shared__ uint32_t lds_st[kWaves][kRB][2][kStage];  // stage: [0] score bits, [1] (query tag, pool id)
@@ -526,7 +532,7 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
                   fenced = true;
                 }
                 // the (just flushed, empty) stage of rb holds the histogram
-                const float T = select_and_compact(a.cand + wbase + (int64_t)q * cap, n, topk,
+                const float T = select_and_compact<kSelectRegs>(a.cand + wbase + (int64_t)q * cap, n, topk,
                                                    lds_st[wave][rb][0], nullptr);
                 cnt_v = lane == q ? topk : cnt_v;
 #pragma unroll
@@ -591,7 +597,7 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
         int32_t* dst = a.idx_out + qr * topk;
         int filled = n;
         if (n > topk) {
-          select_and_compact(a.cand + base, n, topk, lds_st[wave][0][0], dst);  // stages are empty
+          select_and_compact<kSelectRegs>(a.cand + base, n, topk, lds_st[wave][0][0], dst);  // stages are empty
           filled = topk;
         } else {
           const u32x2_t* src = a.cand + base;
@@ -651,10 +657,10 @@ Residency index_residency() {
 }
 
 // Queries per wave, 4 kRB.  kRB = 4 shares each staged key tile among 64
-// queries of a workgroup but needs 246 VGPRs and 81 KB of LDS: two workgroups
-// a CU.  kRB = 2 is held to 168 VGPRs (a few values spill) and needs 53 KB, so
-// a CU holds three; kRB = 1 needs 163 VGPRs and 39 KB, also three, in half-size
-// workgroups.  Measured per call, same ids: at S = 2^20 keys 85.0 ms for kRB = 2
+// queries of a workgroup but needs 248 VGPRs and 81 KB of LDS: two workgroups
+// a CU.  kRB = 2 needs 157 VGPRs and 53 KB, so a CU holds three; kRB = 1 needs
+// 115 VGPRs and 39 KB, four a CU, in half-size workgroups.  Measured per call,
+// same ids: at S = 2^20 keys 85.0 ms for kRB = 2
 // against 98.3 (kRB = 4) and 106.4 (kRB = 1); at 2^17 keys 2.18 against 2.69
 // and 2.49 ms; at 2^15 and 4096 queries kRB = 1 is fastest (0.46 against 0.64
 // ms, 0.086 against 0.14), its grid of 16-query tiles filling the CUs evenly.

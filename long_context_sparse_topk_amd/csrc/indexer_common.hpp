@@ -30,11 +30,11 @@ constexpr int kExactSharedSlots = 64;      // exact-pass grid when the CUs are s
 // with all loads of a lane in flight; a list of up to 64 x kR entries is read
 // once and stays in registers through every pass.  The k-th largest key is
 // found by a radix select over the bits where the keys differ (their OR xor
-// AND), 8 bits per pass, with a per-wave LDS histogram.
+// AND), 8 bits per pass, with a per-wave LDS histogram.  kR is the caller's
+// register budget: with 24 a list of up to 1536 entries is read once, with 8
+// a longer list is read again in every pass.
 
-constexpr int kR = 8;
-constexpr int kChunk = kWave * kR;
-
+template <int kR>
 __device__ __forceinline__ void load_chunk(const u32x2_t* __restrict__ list, int base, int n,
                                            u32x2_t (&e)[kR]) {
   const int lane = lane_id();
@@ -47,8 +47,10 @@ __device__ __forceinline__ void load_chunk(const u32x2_t* __restrict__ list, int
 
 // Steps of a chunk are skipped (wave-uniformly) past the list end, so short
 // lists cost in proportion to their length.
+template <int kR>
 __device__ __forceinline__ float select_and_compact(u32x2_t* __restrict__ list, int n, int k, uint32_t* hist,
                                     int32_t* __restrict__ out) {
+  constexpr int kChunk = kWave * kR;
   const int lane = lane_id();
   const int nch = (n + kChunk - 1) / kChunk;
   u32x2_t e[kR];

@@ -42,6 +42,7 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kKeep32 = 4;        // sampled scores kept per lane and query (32 lanes share one)
+constexpr int kSelectRegs = 8;    // list entries per lane the selection holds in registers
 constexpr int kStage32 = 640;     // stage entries per (wave, row block of 8 queries)
 constexpr int kTileWorst = 8 * kPT;  // most entries one pool tile adds to a stage
 constexpr uint32_t kTag32Shift = 29;   // staged pool id: query (0..7) of the row block in bits 29-31
@@ -550,7 +551,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
                   fenced = true;
                 }
                 // the (just flushed, empty) stage of rb holds the histogram
-                const float T = select_and_compact(a.cand + wbase + (int64_t)q * cap, n, topk,
+                const float T = select_and_compact<kSelectRegs>(a.cand + wbase + (int64_t)q * cap, n, topk,
                                                    lds_st[wave][rb][0], nullptr);
                 cnt_v = lane == q ? topk : cnt_v;
 #pragma unroll
@@ -620,7 +621,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         int32_t* dst = a.idx_out + qr * topk;
         int filled = n;
         if (n > topk) {
-          select_and_compact(a.cand + base, n, topk, lds_st[wave][0][0], dst);  // stages are empty
+          select_and_compact<kSelectRegs>(a.cand + base, n, topk, lds_st[wave][0][0], dst);  // stages are empty
           filled = topk;
         } else {
           const u32x2_t* src = a.cand + base;
