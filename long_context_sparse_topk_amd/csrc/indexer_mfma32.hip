@@ -1,6 +1,5 @@
 // Lightning indexer with a fused per-query top-k on the 32x32 MFMA layout
-// (gfx950): fp8 (OCP e4m3) operands on v_mfma_f32_32x32x64_f8f6f4, or bf16
-// operands on four v_mfma_f32_32x32x16_bf16.
+// (gfx950): fp8 (OCP e4m3) operands on v_mfma_f32_32x32x64_f8f6f4.
 //
 // What is computed is what indexer.hip computes (pages: "SkyRL 将 GLM-5.3-Flash
 // 训练上下文扩至 100 万 token", sections "模型与瓶颈" and "四块优化 1. DSA
@@ -21,15 +20,14 @@
 // (query, pool) pairs with the whole 64-dim contraction: half the matrix-core
 // cycles of bf16 per pair, and half the key bytes per pool (64 B).
 //
-// Precision: the pooled keys and the folded queries w*q are rounded to e4m3
-// (fp8) or bf16; the dot products accumulate in fp32.  For integer indexer
+// Precision: the pooled keys and the folded queries w*q are rounded to e4m3;
+// the dot products accumulate in fp32.  For integer indexer
 // inputs in [-3, 3] every value is exact in e4m3 (w*q is an integer in
 // [-9, 9], a pooled key a multiple of 1/4 in [-3, 3]) and every partial sum is
 // exact in fp32, so the selection equals the exact ranking.
 
 #include <cmath>
 #include <mutex>
-#include <type_traits>
 
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
@@ -48,9 +46,7 @@ constexpr int kTileWorst = 8 * kPT;  // most entries one pool tile adds to a sta
 constexpr uint32_t kTag32Shift = 29;   // staged pool id: query (0..7) of the row block in bits 29-31
 constexpr uint32_t kPool32Mask = (1u << kTag32Shift) - 1u;
 
-// Row bytes of a pooled key: 64 fp8 or 64 bf16 values.
-template <bool kFp8>
-constexpr int row_bytes() { return kFp8 ? 64 : 128; }
+constexpr int kRowBytes = 64;     // a pooled key: 64 e4m3 values
 
 // ---------------------------------------------------------------------------
 // Pooled keys in fp8: kpool8[p] = e4m3(mean of k_idx[4p..4p+3]), 64 bytes a
@@ -97,96 +93,46 @@ __global__ __launch_bounds__(256) void pool_keys_fp8_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// Operands.  The k index of the contraction is the indexer dim: for fp8, lane
-// half h holds dims 32h..32h+31 of its row (A) or column (B); for bf16, step
-// ks of the four 32x32x16 products holds dims 16ks + 8h .. 16ks + 8h + 7.  A
-// and B place a dim in the same (half, byte) slot, which is all the
-// contraction needs.
+// Operands.  The k index of the contraction is the indexer dim: lane half h
+// holds dims 32h..32h+31 of its row (A) or column (B), 32 e4m3 bytes.  A and B
+// place a dim in the same (half, byte) slot, which is all the contraction
+// needs.
 
-template <bool kFp8>
-struct Operand32 {
-  // fp8: 32 bytes; bf16: 4 steps of 8 values
-  typedef typename std::conditional<kFp8, i32x8_t, bf16x8_t[4]>::type type;
-};
-
-// w * q of one (query, head) row for this lane's dims, rounded to the operand type
-template <bool kFp8>
-__device__ __forceinline__ void fold_row(const uint16_t* qrow, float w, bool ok, int h,
-                                         typename Operand32<kFp8>::type& A) {
-  if constexpr (kFp8) {
-    i32x8_t r;
+// w * q of one (query, head) row for this lane's dims, rounded to e4m3
+__device__ __forceinline__ void fold_row(const uint16_t* qrow, float w, bool ok, int h, i32x8_t& A) {
+  i32x8_t r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * h + 8 * j) : u32x4_t{0u, 0u, 0u, 0u};
-      r[2 * j] = (int)pack_fp8x4(bf16_to_f32(v[0] & 0xFFFFu) * w, bf16_to_f32(v[0] >> 16) * w,
-                                 bf16_to_f32(v[1] & 0xFFFFu) * w, bf16_to_f32(v[1] >> 16) * w);
-      r[2 * j + 1] = (int)pack_fp8x4(bf16_to_f32(v[2] & 0xFFFFu) * w, bf16_to_f32(v[2] >> 16) * w,
-                                     bf16_to_f32(v[3] & 0xFFFFu) * w, bf16_to_f32(v[3] >> 16) * w);
-    }
-    A = r;
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * ks + 8 * h) : u32x4_t{0u, 0u, 0u, 0u};
-      u32x4_t o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[j] = pack_bf16x2(bf16_to_f32(v[j] & 0xFFFFu) * w, bf16_to_f32(v[j] >> 16) * w);
-      A[ks] = as_bf16x8(o);
-    }
+  for (int j = 0; j < 4; ++j) {
+    u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * h + 8 * j) : u32x4_t{0u, 0u, 0u, 0u};
+    r[2 * j] = (int)pack_fp8x4(bf16_to_f32(v[0] & 0xFFFFu) * w, bf16_to_f32(v[0] >> 16) * w,
+                               bf16_to_f32(v[1] & 0xFFFFu) * w, bf16_to_f32(v[1] >> 16) * w);
+    r[2 * j + 1] = (int)pack_fp8x4(bf16_to_f32(v[2] & 0xFFFFu) * w, bf16_to_f32(v[2] >> 16) * w,
+                                   bf16_to_f32(v[3] & 0xFFFFu) * w, bf16_to_f32(v[3] >> 16) * w);
   }
+  A = r;
 }
 
 // ---------------------------------------------------------------------------
 // Key tiles in LDS: 64 pools, row-major, XOR-swizzled in 16-byte chunks so that
 // the B-operand reads (8 lanes reading 16 bytes each at a time) hit distinct
-// banks.  fp8: 4 chunks a pool, chunk ch of pool pr at (ch ^ ((pr >> 1) & 3));
-// bf16: 8 chunks a pool, chunk ch at (ch ^ (pr & 7)).
+// banks: 4 chunks a pool, chunk ch of pool pr at (ch ^ ((pr >> 1) & 3)).
 
-template <bool kFp8>
-__device__ __forceinline__ int phys_chunk(int pr, int ch) {
-  return kFp8 ? (ch ^ ((pr >> 1) & 3)) : (ch ^ (pr & 7));
+__device__ __forceinline__ int phys_chunk(int pr, int ch) { return ch ^ ((pr >> 1) & 3); }
+
+__device__ __forceinline__ void read_b(const u32x4_t* kb, int pr, int h, i32x8_t& B) {
+  const u32x4_t lo = kb[pr * 4 + phys_chunk(pr, 2 * h)];
+  const u32x4_t hi = kb[pr * 4 + phys_chunk(pr, 2 * h + 1)];
+  i32x8_t r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  B = r;
 }
 
-template <bool kFp8>
-__device__ __forceinline__ void read_b(const u32x4_t* kb, int pr, int h,
-                                       typename Operand32<kFp8>::type& B) {
-  if constexpr (kFp8) {
-    const u32x4_t lo = kb[pr * 4 + phys_chunk<true>(pr, 2 * h)];
-    const u32x4_t hi = kb[pr * 4 + phys_chunk<true>(pr, 2 * h + 1)];
-    i32x8_t r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    B = r;
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) B[ks] = as_bf16x8(kb[pr * 8 + phys_chunk<false>(pr, 2 * ks + h)]);
-  }
-}
-
-// The MFMA builtins sit in plain (non-template) device functions: in the host
+// The MFMA builtin sits in a plain (non-template) device function: in the host
 // pass, a gfx950-only builtin inside a template would fail the template's
 // substitution and silently drop the kernel's host stub.
-__device__ __forceinline__ f32x16_t mfma_f8_32x32x64(i32x8_t a, i32x8_t b) {
+__device__ __forceinline__ f32x16_t mma32(i32x8_t a, i32x8_t b) {
   const f32x16_t z = {};
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x16_t mfma_bf16_32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-template <bool kFp8>
-__device__ __forceinline__ f32x16_t mma32(const typename Operand32<kFp8>::type& A,
-                                          const typename Operand32<kFp8>::type& B) {
-  if constexpr (kFp8) {
-    return mfma_f8_32x32x64(A, B);
-  } else {
-    const f32x16_t z = {};
-    f32x16_t d = mfma_bf16_32x32x16(A[0], B[0], z);
-    d = mfma_bf16_32x32x16(A[1], B[1], d);
-    d = mfma_bf16_32x32x16(A[2], B[2], d);
-    return mfma_bf16_32x32x16(A[3], B[3], d);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -194,13 +140,12 @@ __device__ __forceinline__ f32x16_t mma32(const typename Operand32<kFp8>::type& 
 // Per-lane query state is indexed [rb][i]: the lane's query 2i + h of row
 // block rb, h = lane / 32 (wave query 8 rb + 2i + h).
 
-template <bool kTwoPhase, int kNRB, bool kFp8>
+template <bool kTwoPhase, int kNRB>
 __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
   constexpr int kQW = 8 * kNRB;              // queries per wave
   constexpr int kQTile = kWaves * kQW;       // queries per workgroup tile
-  constexpr int kChunks = row_bytes<kFp8>() * kPT / 16;   // 16-byte chunks per key tile
+  constexpr int kChunks = kRowBytes * kPT / 16;   // 16-byte chunks per key tile
   constexpr int kDma = kChunks / kThreads;                // DMA loads per thread per tile
-  typedef typename Operand32<kFp8>::type Op;
   __shared__ __align__(16) u32x4_t lds_k[kRing][kChunks];
   __shared__ uint32_t lds_st[kWaves][kNRB][2][kStage32];   // stage: [0] score bits, [1] (tag, pool id)
   __shared__ int lds_np[kWaves];
@@ -222,11 +167,11 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
 #pragma unroll
   for (int j = 0; j < kDma; ++j) {
     const int L = tid + kThreads * j;
-    const int per = row_bytes<kFp8>() / 16;
+    const int per = kRowBytes / 16;
     const int pr = L / per, pc = L % per;
     // physical chunk pc of pool pr holds logical chunk ch with phys_chunk(pr, ch) == pc;
     // the swizzle is an involution for fixed pr
-    dma_off[j] = pr * row_bytes<kFp8>() + phys_chunk<kFp8>(pr, pc) * 16;
+    dma_off[j] = pr * kRowBytes + phys_chunk(pr, pc) * 16;
   }
 
   if (tid == 0) lds_tile = (int)atomicAdd(a.tile_next, 1u);
@@ -241,7 +186,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
     };
 
     // A operands: row c of row block rb -> query 8 rb + c/4, head c%4, weight folded in
-    Op A[kNRB];
+    i32x8_t A[kNRB];
     float cl[kNRB][4][4];
     int nc[kNRB][4];
 #pragma unroll
@@ -252,7 +197,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         const bool ok = qr >= 0 && hd < a.heads;
         const uint16_t* src = a.q_idx + ((ok ? qr : 0) * a.heads + (ok ? hd : 0)) * kDI;
         const float wv = ok ? bf16_to_f32(a.w_idx[qr * a.heads + hd]) : 0.f;
-        fold_row<kFp8>(src, wv, ok, h, A[rb]);
+        fold_row(src, wv, ok, h, A[rb]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -305,8 +250,8 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
     // two tiles ahead (as in indexer.hip)
     auto dma = [&](int tile, int buf) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.kpool8 + (int64_t)tile * kPT * row_bytes<kFp8>()), (short)0,
-          kPT * row_bytes<kFp8>(), kBufferWord3);
+          (void*)(a.kpool8 + (int64_t)tile * kPT * kRowBytes), (short)0, kPT * kRowBytes,
+          kBufferWord3);
 #pragma unroll
       for (int j = 0; j < kDma; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -335,14 +280,14 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         // both column blocks' operands read and both products issued before the
         // first epilogue, which then runs while the second product is in flight
         float sc[kNRB][2][4];
-        Op Bc[2];
-        read_b<kFp8>(kb, c, h, Bc[0]);
-        read_b<kFp8>(kb, 32 + c, h, Bc[1]);
+        i32x8_t Bc[2];
+        read_b(kb, c, h, Bc[0]);
+        read_b(kb, 32 + c, h, Bc[1]);
         f32x16_t xs[kNRB][2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int rb = 0; rb < kNRB; ++rb) xs[rb][cb] = mma32<kFp8>(A[rb], Bc[cb]);
+          for (int rb = 0; rb < kNRB; ++rb) xs[rb][cb] = mma32(A[rb], Bc[cb]);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
@@ -664,10 +609,10 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
 // chains (MFMA results before the epilogue, ballots before branches).
 constexpr int kNRB32 = 1;
 __global__ __launch_bounds__(kThreads, 4) void indexer32_fp8_kernel(KernelArgs a) {
-  indexer32_body<true, kNRB32, true>(a);
+  indexer32_body<true, kNRB32>(a);
 }
 __global__ __launch_bounds__(kThreads, 4) void indexer32_fp8_exact_kernel(KernelArgs a) {
-  indexer32_body<false, kNRB32, true>(a);
+  indexer32_body<false, kNRB32>(a);
 }
 
 // Workgroups the device keeps resident at once, and its CU count (cached per device).
