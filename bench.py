@@ -314,7 +314,7 @@ def main():
     ap.add_argument("--secondary", default="s128k", help="second workload timed in the same run ('' = none)")
     ap.add_argument("--others", default="s4k,s32k,zigzag4",
                     help="further workloads timed in the same run, comma-separated ('' = none)")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle sample size (rows)")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle sample size (rows; about 10 s of host work at S = 1M)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
