@@ -193,6 +193,68 @@ def test_index_sampled_threshold_too_high(unsampled, permute, queries_per_wave):
         assert got[last].tolist() == list(range(26)) + list(range(64, 102))
 
 
+def _operand_rounding(fp8):
+    """(unit roundoff, absolute error floor) of the indexer's operand format:
+    bf16 has 8 significant bits and the fp32 exponent range; OCP e4m3 has 4
+    significant bits and subnormals spaced 2^-9 below 2^-6."""
+    return (2.0 ** -4, 2.0 ** -10) if fp8 else (2.0 ** -8, 0.0)
+
+
+def _score_error_bound(x, kp, fp8):
+    """Bound on |GPU score - exact score| per pool for one query.
+
+    x [H, 64] = w_h * q_h (exact), kp [n, 64] = exact pooled keys.  The GPU
+    rounds both operands once (to bf16 or e4m3) and accumulates in fp32; the
+    clamp of each head is 1-Lipschitz, so per head the error is at most that of
+    the rounded dot product, (2u + u^2) sum|x||k| + a(1 + u) sum(|x| + |k|) +
+    64 a^2, plus fp32 accumulation (64 and 3 terms), summed over the heads."""
+    u, a = _operand_rounding(fp8)
+    ax, ak = np.abs(x), np.abs(kp)
+    prod = ak @ ax.T                                       # [n, H] sum_d |x||k|
+    per_head = ((2 * u + u * u) * prod + a * (1 + u) * (ax.sum(axis=1)[None, :] + ak.sum(axis=1)[:, None])
+                + 64 * a * a)
+    fp32 = 2.0 ** -24 * (70 * prod.sum(axis=1) + 3 * prod.sum(axis=1))
+    return 1.01 * per_head.sum(axis=1) + fp32 + 1e-12
+
+
+def test_index_real_valued_inputs_select_a_valid_top_k(queries_per_wave):
+    # N(0,1) indexer inputs: the operand rounding (bf16, or e4m3 for the fp8
+    # indexer) may reorder pools whose exact scores are close, so the ids are not
+    # compared with the oracle's; instead every row must hold min(k, n_c) distinct
+    # visible pools, ascending, and no pool left out may beat a selected one by
+    # more than the two pools' error bounds: min(s_sel + e_sel) >= max(s_out - e_out).
+    # (On a CPU emulation of the rounding the bf16 bound catches a dropped head, a
+    # missing ReLU or a flipped weight sign in most rows; the e4m3 bound is 16 times
+    # wider and catches only gross errors there: the integer cases grade fp8 exactly.)
+    S, topk = 4100, 64
+    rng = np.random.default_rng(61)
+    q = _bits(rng.standard_normal((S, 4, 64)))
+    k = _bits(rng.standard_normal((S, 64)))
+    w = _bits(rng.standard_normal((S, 4)))
+    fp8 = _INDEX_FP8[0]
+    note(f"index real-valued inputs S={S} topk={topk} qpw={queries_per_wave}")
+    got = gpu_index(q, k, w, topk)
+    qf, wf = O.widen_bf16(q), O.widen_bf16(w)
+    kp = O.pool_keys(O.widen_bf16(k))
+    worst = np.inf
+    for i in range(S):
+        n_c = O.n_complete_pools(i)
+        m = min(topk, n_c)
+        row = got[i]
+        assert (row[m:] == -1).all() and (row[:m] >= 0).all() and (row[:m] < n_c).all(), f"row {i}: {row}"
+        assert (np.diff(row[:m]) > 0).all(), f"row {i}: ids not strictly ascending"
+        if m == 0 or m == n_c:
+            continue
+        s = O.scores_row(qf[i], wf[i], kp, n_c)
+        e = _score_error_bound(qf[i] * wf[i][:, None], kp[:n_c], fp8)
+        sel = np.zeros(n_c, dtype=bool)
+        sel[row[:m]] = True
+        margin = (s[sel] + e[sel]).min() - (s[~sel] - e[~sel]).max()
+        worst = min(worst, margin)
+        assert margin >= 0, f"row {i}: a left-out pool beats a selected one beyond the error bounds"
+    note(f"  smallest margin {worst:.3e}")
+
+
 @pytest.mark.parametrize("heads", [5, 6, 8])
 def test_index_five_to_eight_heads(heads):
     # 5 to 8 indexer heads: two groups of 4 heads per query in the MFMA tile
