@@ -34,6 +34,14 @@ import synthetic as syn  # noqa: E402
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 BF16_PEAK = 2.5e15         # flop/s, dense bf16 MFMA
 FP8_PEAK = 5.0e15          # flop/s, dense fp8 MFMA
+# VALU issue: 256 CUs x 4 SIMDs, one wave64 VALU instruction (16 lanes a cycle, 4 cycles)
+# per SIMD every 4 cycles at 2.4 GHz; MFMA instructions take an issue slot too
+VALU_ISSUE_PEAK = 256 * 4 * 2.4e9 / 4    # wave64 VALU instructions/s
+# the indexer's minimal VALU stream per 64 (query, pool) pairs: the epilogue (4 clamps, 3 adds,
+# 1 compare per pair, one pair a lane) and the MFMA that score them (16x16x32 bf16: 2 per 64
+# pairs; 32x32x64 fp8: 1 per 256 pairs)
+INDEX_EPILOGUE_PER64 = 8
+INDEX_MFMA_PER64 = {"bf16": 2.0, "fp8": 0.25}
 SCALE = 1.0 / np.sqrt(128.0)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 _CSRC = "long_context_sparse_topk_amd/csrc/"
@@ -369,15 +377,24 @@ def main():
     # the indexer beside the dominant kernel (bf16 MFMA-bound), and the fp8 variant (opt-in,
     # dsa_index_topk_fp8) against the fp8 peak and, for comparison, the bf16 one
     ki = kern["indexer_topk_kernel"]
+    def valu_view(kind, seconds):
+        # the same launch against the VALU issue rate: the minimal VALU stream of the scoring
+        # (epilogue + MFMA issue) per second, against VALU_ISSUE_PEAK
+        instr = w["index_pairs"] / 64.0 * (INDEX_EPILOGUE_PER64 + INDEX_MFMA_PER64[kind])
+        return {"bound": "alu", "achieved": round(instr / seconds / 1e9, 2), "peak": VALU_ISSUE_PEAK / 1e9,
+                "unit": "G wave64 VALU instr/s", "frac": round(instr / seconds / VALU_ISSUE_PEAK, 4)}
+
     roofline["indexer"] = {"kernel": "indexer_topk_kernel", "bound": "mfma", "achieved": round(ki["achieved"], 2),
                            "peak": ki["peak"], "unit": "TFLOP/s", "frac": round(ki["achieved"] / ki["peak"], 4),
                            "traffic": measured_traffic("indexer_topk_kernel", wl.name),
-                           "ms_per_launch": round(ki["s"] * 1e3, 3)}
+                           "ms_per_launch": round(ki["s"] * 1e3, 3),
+                           "valu": valu_view("bf16", avg["index"])}
     f8 = w["index_flop"] / avg["index_fp8"] / 1e12
     kernels["indexer32_fp8_kernel"] = {"ms": round(avg["index_fp8"] * 1e3, 3), "achieved": round(f8, 2),
                                        "unit": "TFLOP/s", "frac": round(f8 * 1e12 / FP8_PEAK, 4),
                                        "frac_of_bf16_peak": round(f8 * 1e12 / BF16_PEAK, 4),
-                                       "traffic": measured_traffic("indexer32_fp8_kernel", wl.name)}
+                                       "traffic": measured_traffic("indexer32_fp8_kernel", wl.name),
+                                       "valu": valu_view("fp8", avg["index_fp8"])}
 
     secondary = None
     if args.secondary and args.secondary != wl.name:
