@@ -86,7 +86,21 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 
 constexpr int kSampleKeep = 8;   // sampled scores kept per lane and query
-constexpr int kStage = kIndexStage;
+
+// Survivor-stage entries per (wave, row block) and key-ring buffers, per
+// sub-tile.  The 32-query sub-tile (kRB = 2) is sized for four workgroups a CU
+// (four waves a SIMD): 128 registers and 40 KB of LDS, from a two-buffer key
+// ring (16 KB, loads one tile ahead) and 376-entry stages (24 KB), with each
+// column block's products and epilogue done before the next block's operands
+// are read.  Measured at S = 2^20 (same ids): 77.6 ms against 85.9 ms at three
+// workgroups a CU (three-buffer ring, 440-entry stages, all four blocks'
+// products first, 157 registers); S = 2^17: 2.01 against 2.28 ms.  (The
+// three-buffer ring issues loads two tiles ahead, but the barrier's release
+// fence waits for LDS-destined loads, so either ring keeps one tile in flight.)
+template <int kRB>
+constexpr int stage_entries() { return kRB == 2 ? 376 : kIndexStage; }
+template <int kRB>
+constexpr int ring_buffers() { return kRB == 2 ? 2 : kRing; }
 constexpr uint32_t kTagShift = 30;               // staged pool id: query (0..3) in bits 30-31
 constexpr uint32_t kPoolMask = (1u << kTagShift) - 1u;
 
@@ -121,7 +135,9 @@ __device__ __forceinline__ bf16x8_t fold_weight(u32x4_t q, float w) {
 // order).  Keeping global stores out of the scoring loop keeps the prefetch
 // wait exact (loads and stores share one completion counter).
 template <bool kTwoPhase, int kRB, int kHG>
-__global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kernel(KernelArgs a) {
+  constexpr int kStage = stage_entries<kRB>();
+  constexpr int kRingN = ring_buffers<kRB>();
   constexpr int kQW = 4 * kRB;        // queries per wave (kRB row blocks of 4)
   // list entries per lane the selection holds in registers: the 64-query
   // sub-tile runs one wave a SIMD beside the forward, where a selection's
@@ -130,7 +146,7 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
   // (S = 2^17: 2.20 ms against 2.34 with 24)
   constexpr int kSelectRegs = kRB == 4 ? 24 : 8;
   constexpr int kQTile = kWaves * kQW;  // queries per workgroup tile
-  __shared__ __align__(16) u32x4_t lds_k[kRing][kPT * 8];   // ring of (64 pools x 128 B), swizzled
+  __shared__ __align__(16) u32x4_t lds_k[kRingN][kPT * 8];   // ring of (64 pools x 128 B), swizzled
   __shared__ uint32_t lds_st[kWaves][kRB][2][kStage];  // stage: [0] score bits, [1] (query tag, pool id)
   __shared__ int lds_np[kWaves];
   __shared__ uint32_t lds_fail[kWaves];
@@ -236,9 +252,9 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
     const int64_t wbase = ((int64_t)blockIdx.x * kQTile + kQW * wave) * cap;
 
     // Pool-key tiles go straight from HBM to LDS (buffer loads with the LDS
-    // destination) through a ring of kRing buffers, issued two tiles ahead of
-    // the one being scored.  (The workgroup barrier releases LDS, and these
-    // loads write LDS, so the compiler waits for all of them before each
+    // destination) through a ring of kRingN buffers, issued kRingN - 1 tiles
+    // ahead of the one being scored.  (The workgroup barrier releases LDS, and
+    // these loads write LDS, so the compiler waits for all of them before each
     // barrier: a tile's loads have one tile's scoring time to land.)  Lane l
     // of a load instruction writes LDS chunk
     // (base + l); its source offset is chosen so that LDS row pr, chunk ch
@@ -259,33 +275,47 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
     // Stream pool tiles first, first+step, ... < ntp.  Per tile i: wait for
     // this thread's part of tile i and meet at the barrier (tile i is then in
     // LDS and every wave is done with tile i-1's buffer), run
-    // `before_load(i)` (it may issue global stores), start tile i+2, and
+    // `before_load(i)` (it may issue global stores), start tile i+kAhead, and
     // hand the tile's scores to `consume(sc, pt0)` (-inf where a pool is not
     // causal for the query).  Loads complete in order among themselves, so
     // with tile i+1's two loads younger than tile i's, "at most 2
     // outstanding" means tile i has landed, whatever the stores do.  Tile 0
     // of a stream is always loaded (in bounds: the keys are padded to >= 1
     // tile).
+    constexpr int kAhead = kRingN - 1;
+    // epilogue: clamp each head to the side of its weight, sum the heads
+    auto head_sum = [&](const f32x4_t (&x)[kHG], int rb) -> float {
+      float hs[kHG];
+#pragma unroll
+      for (int hg = 0; hg < kHG; ++hg) {
+        const float s01 = __builtin_amdgcn_fmed3f(x[hg][0], cl[rb][hg][0], 0.f) +
+                          __builtin_amdgcn_fmed3f(x[hg][1], cl[rb][hg][1], 0.f);
+        const float s23 = __builtin_amdgcn_fmed3f(x[hg][2], cl[rb][hg][2], 0.f) +
+                          __builtin_amdgcn_fmed3f(x[hg][3], cl[rb][hg][3], 0.f);
+        hs[hg] = s01 + s23;
+      }
+      if constexpr (kHG == 1) return hs[0];
+      else return hs[0] + hs[1];
+    };
     auto stream = [&](int first, int step, auto&& before_load, auto&& consume) {
       const int nt = first < ntp ? (ntp - first + step - 1) / step : 0;
       dma(first < ntp ? first : 0, 0);
-      if (nt > 1) dma(first + step, 1);
-      int buf = 0, lbuf = 2;  // buffer of tile i, and of tile i+2 ((buf + 2) mod kRing)
+      if (kAhead == 2 && nt > 1) dma(first + step, 1);
+      int buf = 0;  // buffer of tile i; tile i + kAhead goes to (buf + kAhead) mod kRingN
       for (int i = 0; i < nt; ++i) {
         const int pt0 = (first + i * step) * kPT;
-        if (i + 1 < nt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt2);
+        if (kAhead == 2 && i + 1 < nt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt2);
         else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         lds_barrier();
         const u32x4_t* kb = lds_k[buf];
         before_load(i);
-        if (i + 2 < nt) dma(first + (i + 2) * step, lbuf);
-        buf = buf == kRing - 1 ? 0 : buf + 1;
-        lbuf = lbuf == kRing - 1 ? 0 : lbuf + 1;
+        if (i + kAhead < nt) dma(first + (i + kAhead) * step, buf == 0 ? kRingN - 1 : buf - 1);
+        buf = buf == kRingN - 1 ? 0 : buf + 1;
 
-        // 16 output blocks of 16 (query x head) rows x 16 pools per head group
-        f32x4_t acc[kRB][kHG][4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        // 16 output blocks of 16 (query x head) rows x 16 pools per head group:
+        // column block cb holds pools 16 cb .. 16 cb + 15 of the tile
+        float sc[kRB][4];
+        auto products = [&](int cb, f32x4_t (&x)[kRB][kHG]) {
           const int pr = 16 * cb + c16;
           const bf16x8_t B0 = as_bf16x8(kb[pr * 8 + (g ^ (pr & 7))]);
           const bf16x8_t B1 = as_bf16x8(kb[pr * 8 + ((4 + g) ^ (pr & 7))]);
@@ -294,28 +324,27 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 3 : 2) void indexer_topk_kerne
 #pragma unroll
             for (int hg = 0; hg < kHG; ++hg) {
               f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-              acc[rb][hg][cb] = mfma32(A[rb][hg][1], B1, mfma32(A[rb][hg][0], B0, z));
+              x[rb][hg] = mfma32(A[rb][hg][1], B1, mfma32(A[rb][hg][0], B0, z));
             }
-        }
-        // epilogue: clamp each head to the side of its weight, sum the heads
-        float sc[kRB][4];
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
+        };
+        if constexpr (kRB == 2) {
+          // one column block at a time: fewer live registers, four waves a SIMD
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            float hs[kHG];
+            f32x4_t x[kRB][kHG];
+            products(cb, x);
 #pragma unroll
-            for (int hg = 0; hg < kHG; ++hg) {
-              const f32x4_t x = acc[rb][hg][cb];
-              const float s01 = __builtin_amdgcn_fmed3f(x[0], cl[rb][hg][0], 0.f) +
-                                __builtin_amdgcn_fmed3f(x[1], cl[rb][hg][1], 0.f);
-              const float s23 = __builtin_amdgcn_fmed3f(x[2], cl[rb][hg][2], 0.f) +
-                                __builtin_amdgcn_fmed3f(x[3], cl[rb][hg][3], 0.f);
-              hs[hg] = s01 + s23;
-            }
-            if constexpr (kHG == 1) sc[rb][cb] = hs[0];
-            else sc[rb][cb] = hs[0] + hs[1];
+            for (int rb = 0; rb < kRB; ++rb) sc[rb][cb] = head_sum(x[rb], rb);
           }
+        } else {
+          // every block's products first, then the epilogues (one or two waves a SIMD)
+          f32x4_t acc[4][kRB][kHG];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) products(cb, acc[cb]);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) sc[rb][cb] = head_sum(acc[cb][rb], rb);
         }
         // causal pool mask, only on tiles some query of the wave sees in part
         if (pt0 + kPT > ncmin) {
@@ -658,9 +687,10 @@ Residency index_residency() {
 
 // Queries per wave, 4 kRB.  kRB = 4 shares each staged key tile among 64
 // queries of a workgroup but needs 248 VGPRs and 81 KB of LDS: two workgroups
-// a CU.  kRB = 2 needs 157 VGPRs and 53 KB, so a CU holds three; kRB = 1 needs
-// 115 VGPRs and 39 KB, four a CU, in half-size workgroups.  Measured per call,
-// same ids: at S = 2^20 keys 85.0 ms for kRB = 2
+// a CU.  kRB = 2 is held to 128 VGPRs and 40 KB (see stage_entries), four a
+// CU; kRB = 1 needs 115 VGPRs and 39 KB, also four, in half-size workgroups.
+// Measured per call, same ids (kRB = 2 at three workgroups a CU, before it
+// fitted four): at S = 2^20 keys 85.0 ms for kRB = 2
 // against 98.3 (kRB = 4) and 106.4 (kRB = 1); at 2^17 keys 2.18 against 2.69
 // and 2.49 ms; at 2^15 and 4096 queries kRB = 1 is fastest (0.46 against 0.64
 // ms, 0.086 against 0.14), its grid of 16-query tiles filling the CUs evenly.
