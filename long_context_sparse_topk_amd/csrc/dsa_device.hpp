@@ -123,14 +123,80 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// ---------------------------------------------------------------------------
+// Cross-lane steps on DPP (data-parallel primitives: a VALU operand read from
+// another lane of the same row of 16), which need no LDS round trip as
+// ds_bpermute (what __shfl lowers to) does.  dpp_ctrl values of this ISA:
+// quad_perm [1,0,3,2] and [2,3,0,1] exchange lanes 1 and 2 apart within each
+// quad, row_half_mirror reverses each half row of 8 lanes, row_mirror each
+// row; after the first k of these four steps a lane holds the combination of
+// 2^k lanes of its row.  row_shr:n reads the lane n before (0 before the row
+// start, with bound_ctrl); row_bcast:15 / :31 read lane 15 of the row before /
+// lane 31, in the rows that row_mask enables.
+constexpr int kDppQuadSwap1 = 0xB1;
+constexpr int kDppQuadSwap2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr3 = 0x113;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int kCtrl, int kRowMask = 0xF, int kBankMask = 0xF, bool kBoundZero = false>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, kBankMask, kBoundZero);
+}
+
+// every lane of a row of 16 gets op over the row's 16 values
+template <class Op>
+__device__ __forceinline__ int row_reduce16(int v, Op op) {
+  v = op(v, dpp<kDppQuadSwap1>(v));
+  v = op(v, dpp<kDppQuadSwap2>(v));
+  v = op(v, dpp<kDppRowHalfMirror>(v));
+  return op(v, dpp<kDppRowMirror>(v));
+}
+
+__device__ __forceinline__ int row_sum16(int v) {
+  return row_reduce16(v, [](int x, int y) { return x + y; });
+}
+
+// op over the wave: the rows' results combined from lanes 0, 16, 32, 48
+template <class Op>
+__device__ __forceinline__ int wave_reduce(int v, Op op) {
+  const int r = row_reduce16(v, op);
+  return op(op(__builtin_amdgcn_readlane(r, 0), __builtin_amdgcn_readlane(r, 16)),
+            op(__builtin_amdgcn_readlane(r, 32), __builtin_amdgcn_readlane(r, 48)));
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+  return wave_reduce(v, [](int x, int y) { return x > y ? x : y; });
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+  return wave_reduce(v, [](int x, int y) { return x < y ? x : y; });
+}
+
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-  for (int o = 32; o >= 1; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o, kWave);
-  return v;
+  return (uint32_t)wave_reduce((int)v, [](int x, int y) { return x | y; });
 }
 
 __device__ __forceinline__ uint32_t wave_and(uint32_t v) {
-  for (int o = 32; o >= 1; o >>= 1) v &= (uint32_t)__shfl_xor((int)v, o, kWave);
-  return v;
+  return (uint32_t)wave_reduce((int)v, [](int x, int y) { return x & y; });
+}
+
+// inclusive prefix sum over the 64 lanes: sums of 4 within a row, then of 8
+// and 16 (lanes 4.. and 8.. of each row), then the earlier rows' totals
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  int s = v + dpp<kDppRowShr1, 0xF, 0xF, true>(v);
+  s += dpp<kDppRowShr2, 0xF, 0xF, true>(v);
+  s += dpp<kDppRowShr3, 0xF, 0xF, true>(v);
+  s += dpp<kDppRowShr4, 0xF, 0xE>(s);
+  s += dpp<kDppRowShr8, 0xF, 0xC>(s);
+  s += dpp<kDppRowBcast15, 0xA>(s);
+  return s + dpp<kDppRowBcast31, 0xC>(s);
 }
 
 }  // namespace dsa

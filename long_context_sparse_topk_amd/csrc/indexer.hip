@@ -164,6 +164,10 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
   const int64_t nrow = kTwoPhase ? a.Sq : (int64_t)__builtin_amdgcn_readfirstlane(*a.nrows);
   const int64_t ntiles = (nrow + kQTile - 1) / kQTile;
   const uint32_t lane_tag = ((uint32_t)g << kTagShift) | (uint32_t)c16;
+  // byte offsets in a key tile of this lane's two B-operand chunks of column
+  // block 0 (pool c16, key chunks g and 4 + g, swizzled); block cb is 2048 B on
+  const int b_off0 = c16 * 128 + ((g ^ (c16 & 7)) << 4);
+  const int b_off1 = c16 * 128 + (((4 + g) ^ (c16 & 7)) << 4);
   int dma_off[2];  // byte offset in a key tile of the chunk this thread's loads bring
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -229,14 +233,11 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
     int ncm = nc[0];
 #pragma unroll
     for (int rb = 1; rb < kRB; ++rb) ncm = max(ncm, nc[rb]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ncm = max(ncm, __shfl_xor(ncm, o, kWave));
+    ncm = wave_max(ncm);
     int ncmin = nc[0];
 #pragma unroll
     for (int rb = 1; rb < kRB; ++rb) ncmin = min(ncmin, nc[rb]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ncmin = min(ncmin, __shfl_xor(ncmin, o, kWave));
-    ncmin = uniform(ncmin);
+    ncmin = wave_min(ncmin);
     if (lane == 0) lds_np[wave] = ncm;
     lds_barrier();
     if (tid == 0) lds_tile = (int)atomicAdd(a.tile_next, 1u);  // read after the tile
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
         if (kAhead == 2 && i + 1 < nt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt2);
         else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         lds_barrier();
-        const u32x4_t* kb = lds_k[buf];
+        const char* kb = reinterpret_cast<const char*>(lds_k[buf]);
         before_load(i);
         if (i + kAhead < nt) dma(first + (i + kAhead) * step, buf == 0 ? kRingN - 1 : buf - 1);
         buf = buf == kRingN - 1 ? 0 : buf + 1;
@@ -316,9 +317,8 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
         // column block cb holds pools 16 cb .. 16 cb + 15 of the tile
         float sc[kRB][4];
         auto products = [&](int cb, f32x4_t (&x)[kRB][kHG]) {
-          const int pr = 16 * cb + c16;
-          const bf16x8_t B0 = as_bf16x8(kb[pr * 8 + (g ^ (pr & 7))]);
-          const bf16x8_t B1 = as_bf16x8(kb[pr * 8 + ((4 + g) ^ (pr & 7))]);
+          const bf16x8_t B0 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + b_off0 + 2048 * cb));
+          const bf16x8_t B1 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kb + b_off1 + 2048 * cb));
 #pragma unroll
           for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
@@ -416,32 +416,43 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
               if ((j & d) == 0) cx(b[j], b[j + d]);
         }
       });
-      // r-th best of the 16 lanes x kSampleKeep kept scores of each query:
-      // the largest key v with at least r kept keys >= v, bit by bit
+      // r-th best of the 16 lanes (a DPP row) x kSampleKeep kept scores of
+      // each query: the largest key v with at least r kept keys >= v, bit by
+      // bit from the top, for both ranks at once.  Only bits where some keys
+      // of the wave differ are searched: a bit every key of the row shares is
+      // the answer's too, and starting from the row's common one-bits leaves
+      // each remaining test (keys >= candidate) as in the full search.
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         uint32_t kk[kSampleKeep];
+        uint32_t ko = 0u, ka = 0xFFFFFFFFu;
 #pragma unroll
-        for (int j = 0; j < kSampleKeep; ++j) kk[j] = order_key(best[rb][j] + 0.f);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int r = rq[m][rb];
-          uint32_t pre_k = 0u;
-          for (int b = 31; b >= 0; --b) {
-            const uint32_t cand_k = pre_k | (1u << b);
-            int c = 0;
-#pragma unroll
-            for (int j = 0; j < kSampleKeep; ++j) c += kk[j] >= cand_k ? 1 : 0;
-            c += __shfl_xor(c, 1, kWave);
-            c += __shfl_xor(c, 2, kWave);
-            c += __shfl_xor(c, 4, kWave);
-            c += __shfl_xor(c, 8, kWave);
-            if (c >= r) pre_k = cand_k;
-          }
-          const float t = r > 0 ? float_below(key_to_float(pre_k)) : NEG_INF;
-          if (m == 0) tau[rb] = t;
-          else tau2[rb] = t;
+        for (int j = 0; j < kSampleKeep; ++j) {
+          kk[j] = order_key(best[rb][j] + 0.f);
+          ko |= kk[j];
+          ka &= kk[j];
         }
+        ka = (uint32_t)row_reduce16((int)ka, [](int x, int y) { return x & y; });
+        uint32_t bits = wave_or(ko ^ ka);   // wave-uniform
+        const int r0 = rq[0][rb], r1 = rq[1][rb];
+        uint32_t p0 = ka, p1 = ka;
+        while (bits != 0u) {
+          const uint32_t bit = 1u << (31 - __builtin_clz(bits));
+          bits ^= bit;
+          const uint32_t c0k = p0 | bit, c1k = p1 | bit;
+          int c0 = 0, c1 = 0;
+#pragma unroll
+          for (int j = 0; j < kSampleKeep; ++j) {
+            c0 += kk[j] >= c0k ? 1 : 0;
+            c1 += kk[j] >= c1k ? 1 : 0;
+          }
+          c0 = row_sum16(c0);
+          c1 = row_sum16(c1);
+          if (c0 >= r0) p0 = c0k;
+          if (c1 >= r1) p1 = c1k;
+        }
+        tau[rb] = r0 > 0 ? float_below(key_to_float(p0)) : NEG_INF;
+        tau2[rb] = r1 > 0 ? float_below(key_to_float(p1)) : NEG_INF;
       }
     }
 
@@ -616,7 +627,7 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
         int ncr = nc[0];
 #pragma unroll
         for (int r = 1; r < kRB; ++r) ncr = r == rb ? nc[r] : ncr;
-        const int need = min(topk, __shfl(ncr, 16 * (q & 3), kWave));
+        const int need = min(topk, __builtin_amdgcn_readlane(ncr, 16 * (q & 3)));
         if (kTwoPhase && n < need) {  // threshold estimate too high
           if (attempt == 0) failed |= 1u << q;
           else if (lane == 0) a.fb_rows[atomicAdd(a.fb_count, 1u)] = (int32_t)qr;

@@ -102,12 +102,9 @@ __device__ __forceinline__ float select_and_compact(u32x2_t* __restrict__ list, 
       const int h0 = (int)hist[lane * 4 + 0], h1 = (int)hist[lane * 4 + 1];
       const int h2 = (int)hist[lane * 4 + 2], h3 = (int)hist[lane * 4 + 3];
       const int tot = h0 + h1 + h2 + h3;
-      int suf = tot;  // inclusive suffix sum over lanes (bins ascending with lane)
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int t = __shfl_down(suf, off, kWave);
-        if (lane + off < kWave) suf += t;
-      }
+      // inclusive suffix sum over lanes (bins ascending with lane)
+      const int pre = wave_prefix_sum(tot);
+      const int suf = __builtin_amdgcn_readlane(pre, kWave - 1) - pre + tot;
       const uint64_t ge = ballot(suf >= rem);
       const int L = 63 - __clzll((long long)ge);
       const int s3 = suf - tot + h3, s2 = s3 + h2, s1 = s2 + h1;
@@ -116,8 +113,8 @@ __device__ __forceinline__ float select_and_compact(u32x2_t* __restrict__ list, 
       else if (s2 >= rem) { d = 2; above = s2 - h2; }
       else if (s1 >= rem) { d = 1; above = s1 - h1; }
       else { d = 0; above = suf - h0; }
-      const int digit = __shfl(lane * 4 + d, L, kWave);
-      above = __shfl(above, L, kWave);
+      const int digit = __builtin_amdgcn_readlane(lane * 4 + d, L);
+      above = __builtin_amdgcn_readlane(above, L);
       rem -= above;
       prefix |= (uint32_t)digit << shift;
       top = shift;

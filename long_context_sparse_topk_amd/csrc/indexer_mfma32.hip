@@ -119,9 +119,18 @@ __device__ __forceinline__ void fold_row(const uint16_t* qrow, float w, bool ok,
 
 __device__ __forceinline__ int phys_chunk(int pr, int ch) { return ch ^ ((pr >> 1) & 3); }
 
-__device__ __forceinline__ void read_b(const u32x4_t* kb, int pr, int h, i32x8_t& B) {
-  const u32x4_t lo = kb[pr * 4 + phys_chunk(pr, 2 * h)];
-  const u32x4_t hi = kb[pr * 4 + phys_chunk(pr, 2 * h + 1)];
+// The lane's B operand of one column block: pool pr of the tile, dims of lane
+// half h.  `off_lo` / `off_hi` are the byte offsets of its two chunks for
+// pr = lane % 32 (b_offsets); column block 1 (pr + 32) is 2048 bytes on, with
+// the same swizzle.
+__device__ __forceinline__ void b_offsets(int pr, int h, int& off_lo, int& off_hi) {
+  off_lo = (pr * 4 + phys_chunk(pr, 2 * h)) * 16;
+  off_hi = (pr * 4 + phys_chunk(pr, 2 * h + 1)) * 16;
+}
+
+__device__ __forceinline__ void read_b(const char* kb, int off_lo, int off_hi, i32x8_t& B) {
+  const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(kb + off_lo);
+  const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(kb + off_hi);
   i32x8_t r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   B = r;
@@ -163,6 +172,12 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
   const float POS_INF = __builtin_huge_valf();
   const int64_t nrow = kTwoPhase ? a.Sq : (int64_t)__builtin_amdgcn_readfirstlane(*a.nrows);
   const int64_t ntiles = (nrow + kQTile - 1) / kQTile;
+  int b_lo, b_hi;     // B-operand chunk offsets of column block 0
+  b_offsets(c, h, b_lo, b_hi);
+  // staged pool id: pool | (query of the row block) << kTag32Shift; the lane's
+  // part (pool c, lane half h) here, the tile's and the query pair's part
+  // (wave-uniform) added per staged block
+  const uint32_t lane_tag = (uint32_t)c | ((uint32_t)h << kTag32Shift);
   int dma_off[kDma];  // byte offset in a key tile of the chunk this thread's loads bring
 #pragma unroll
   for (int j = 0; j < kDma; ++j) {
@@ -224,12 +239,8 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         ncm = max(ncm, nc[rb][i]);
         ncmin = min(ncmin, nc[rb][i]);
       }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      ncm = max(ncm, __shfl_xor(ncm, o, kWave));
-      ncmin = min(ncmin, __shfl_xor(ncmin, o, kWave));
-    }
-    ncmin = uniform(ncmin);
+    ncm = wave_max(ncm);
+    ncmin = wave_min(ncmin);
     if (lane == 0) lds_np[wave] = ncm;
     lds_barrier();
     if (tid == 0) lds_tile = (int)atomicAdd(a.tile_next, 1u);  // read after the tile
@@ -271,7 +282,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         if (it + 1 < nt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt2);
         else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         lds_barrier();
-        const u32x4_t* kb = lds_k[buf];
+        const char* kb = reinterpret_cast<const char*>(lds_k[buf]);
         before_load(it);
         if (it + 2 < nt) dma(first + (it + 2) * step, lbuf);
         buf = buf == kRing - 1 ? 0 : buf + 1;
@@ -281,8 +292,8 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         // first epilogue, which then runs while the second product is in flight
         float sc[kNRB][2][4];
         i32x8_t Bc[2];
-        read_b(kb, c, h, Bc[0]);
-        read_b(kb, 32 + c, h, Bc[1]);
+        read_b(kb, b_lo, b_hi, Bc[0]);
+        read_b(kb + 2048, b_lo, b_hi, Bc[1]);
         f32x16_t xs[kNRB][2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
@@ -378,35 +389,47 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
           }
       });
       // r-th best of the 32 lanes x kKeep32 kept scores of each query: the
-      // largest key v with at least r kept keys >= v, bit by bit; the counts of
-      // both lane halves (two queries) come from one ballot per kept score
+      // largest key v with at least r kept keys >= v, bit by bit from the top,
+      // for both ranks at once; the counts of both lane halves (two queries)
+      // come from one ballot per kept score.  Only bits where some keys of the
+      // wave differ are searched: a bit every key shares is the answer's too,
+      // and starting from the common one-bits leaves each remaining test as in
+      // the full search.
 #pragma unroll
       for (int rb = 0; rb < kNRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           uint32_t kk[kKeep32];
+          uint32_t ko = 0u, ka = 0xFFFFFFFFu;
 #pragma unroll
-          for (int j = 0; j < kKeep32; ++j) kk[j] = order_key(best[rb][i][j] + 0.f);
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const int r = rq[m][rb][i];
-            uint32_t pre_k = 0u;
-            for (int b = 31; b >= 0; --b) {
-              const uint32_t cand_k = pre_k | (1u << b);
-              int lo = 0, hi = 0;
-#pragma unroll
-              for (int j = 0; j < kKeep32; ++j) {
-                const uint64_t M = ballot(kk[j] >= cand_k);
-                lo += __popc((uint32_t)M);
-                hi += __popc((uint32_t)(M >> 32));
-              }
-              const int cnt = h ? hi : lo;
-              if (cnt >= r) pre_k = cand_k;
-            }
-            const float t = r > 0 ? float_below(key_to_float(pre_k)) : NEG_INF;
-            if (m == 0) tau[rb][i] = t;
-            else tau2[rb][i] = t;
+          for (int j = 0; j < kKeep32; ++j) {
+            kk[j] = order_key(best[rb][i][j] + 0.f);
+            ko |= kk[j];
+            ka &= kk[j];
           }
+          ka = wave_and(ka);                 // wave-uniform
+          uint32_t bits = wave_or(ko) ^ ka;
+          const int r0 = rq[0][rb][i], r1 = rq[1][rb][i];
+          uint32_t p0 = ka, p1 = ka;
+          while (bits != 0u) {
+            const uint32_t bit = 1u << (31 - __builtin_clz(bits));
+            bits ^= bit;
+            const uint32_t c0k = p0 | bit, c1k = p1 | bit;
+            int lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
+#pragma unroll
+            for (int j = 0; j < kKeep32; ++j) {
+              const uint64_t M0 = ballot(kk[j] >= c0k);
+              const uint64_t M1 = ballot(kk[j] >= c1k);
+              lo0 += __popc((uint32_t)M0);
+              hi0 += __popc((uint32_t)(M0 >> 32));
+              lo1 += __popc((uint32_t)M1);
+              hi1 += __popc((uint32_t)(M1 >> 32));
+            }
+            if ((h ? hi0 : lo0) >= r0) p0 = c0k;
+            if ((h ? hi1 : lo1) >= r1) p1 = c1k;
+          }
+          tau[rb][i] = r0 > 0 ? float_below(key_to_float(p0)) : NEG_INF;
+          tau2[rb][i] = r1 > 0 ? float_below(key_to_float(p1)) : NEG_INF;
         }
     }
 
@@ -527,7 +550,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
                       const int slot = nst[rb] + mbcnt(M);
                       uint32_t* st = &lds_st[wave][rb][0][slot];
                       st[0] = __float_as_uint(sc[rb][cb][i]);
-                      st[kStage32] = (uint32_t)(pt0 + 32 * cb + c) | ((uint32_t)(2 * i + h) << kTag32Shift);
+                      st[kStage32] = ((uint32_t)(pt0 + 32 * cb) + ((uint32_t)i << (kTag32Shift + 1))) | lane_tag;
                     }
                     nst[rb] += __popcll(M);
                   }
@@ -555,7 +578,7 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
         for (int rb = 0; rb < kNRB; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (8 * rb + 2 * i == (q & ~1)) ncq = __shfl(nc[rb][i], 32 * (q & 1), kWave);
+            if (8 * rb + 2 * i == (q & ~1)) ncq = __builtin_amdgcn_readlane(nc[rb][i], 32 * (q & 1));
         const int need = min(topk, ncq);
         if (kTwoPhase && n < need) {  // threshold estimate too high
           if (attempt == 0) failed |= 1u << q;

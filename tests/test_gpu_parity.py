@@ -193,6 +193,23 @@ def test_index_sampled_threshold_too_high(unsampled, permute, queries_per_wave):
         assert got[last].tolist() == list(range(26)) + list(range(64, 102))
 
 
+@pytest.mark.parametrize("unsampled", [125, 10])
+def test_index_rows_at_one_position_threshold_trap(unsampled, queries_per_wave):
+    # 512 query rows, all at the last of 16384 key positions (q_pos constant):
+    # every query tile has the same 64-tile causal range, sampled on the trap's
+    # tiles 0, 8, 16, ..., so every row retries (unsampled = 125) or needs the
+    # exact pass (10); a workgroup's rows all take the same path.
+    Sq, Sk, topk = 512, 16384, 64
+    k_idx = _threshold_trap_keys(Sk, unsampled)
+    q = _bits(np.ones((Sq, 4, 64), np.float32))
+    w = _bits(np.ones((Sq, 4), np.float32))
+    pos = np.full(Sq, Sk - 1, dtype=np.int64)
+    note(f"index rows at one position, threshold trap unsampled={unsampled} qpw={queries_per_wave}")
+    got = gpu_index(q, k_idx, w, topk, q_pos=pos)
+    ref = O.index_topk(q, k_idx, w, pos, topk)
+    assert_idx_equal(f"idx one-position trap {unsampled}", got, ref)
+
+
 def _operand_rounding(fp8):
     """(unit roundoff, absolute error floor) of the indexer's operand format:
     bf16 has 8 significant bits and the fp32 exponent range; OCP e4m3 has 4
