@@ -142,9 +142,11 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
   // list entries per lane the selection holds in registers: the 64-query
   // sub-tile runs one wave a SIMD beside the forward, where a selection's
   // list re-reads are exposed (S = 2^20 pipelined: 197.1 ms with 24, 202.0
-  // with 8); the others keep 8 and fit their registers without spilling
-  // (S = 2^17: 2.20 ms against 2.34 with 24)
-  constexpr int kSelectRegs = kRB == 4 ? 24 : 8;
+  // with 8); the 16-query one (short calls, where k/n is large and lists
+  // compact often) keeps 16 within 128 registers (S = 2^15, k = 512: 0.39-0.41
+  // against 0.43 ms with 8); the others keep 8, which fits their registers
+  // without spilling (S = 2^17: 2.20 ms against 2.34 with 24)
+  constexpr int kSelectRegs = kRB == 4 ? 24 : (kRB == 1 && kHG == 1 ? 16 : 8);
   constexpr int kQTile = kWaves * kQW;  // queries per workgroup tile
   __shared__ __align__(16) u32x4_t lds_k[kRingN][kPT * 8];   // ring of (64 pools x 128 B), swizzled
   __shared__ uint32_t lds_st[kWaves][kRB][2][kStage];  // stage: [0] score bits, [1] (query tag, pool id)
