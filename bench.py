@@ -158,6 +158,16 @@ class Layer:
                      q_pos=self.q_pos, out=self.idx, ws=self.ws_idx, fp8=True)
         ev[1].record()
 
+    def index_rows(self, fp8=False):
+        """One more (untimed) separate indexer call and its row statistics: rows whose first
+        sampled threshold failed (scored again with the wider margin) and rows the exact
+        pass scored."""
+        t, wl = self.t, self.wl
+        D.index_topk(t["q_idx"], t["k_idx"], t["w_idx"], topk=wl.topk, q_chunk=wl.q_chunk,
+                     q_pos=self.q_pos, out=self.idx, ws=self.ws_idx, fp8=fp8)
+        retried, exact = D.index_topk_stats(self.ws_idx, Sq=wl.sq, Sk=wl.sk, topk=wl.topk)
+        return {"retried": retried, "exact_pass": exact, "of": wl.sq}
+
     def kernels(self, ev):
         """The same work as separate entry-point calls, one after the other on the current
         stream (the stream every kernel of these calls is launched on), with events around
@@ -388,13 +398,15 @@ def main():
                            "peak": ki["peak"], "unit": "TFLOP/s", "frac": round(ki["achieved"] / ki["peak"], 4),
                            "traffic": measured_traffic("indexer_topk_kernel", wl.name),
                            "ms_per_launch": round(ki["s"] * 1e3, 3),
-                           "valu": valu_view("bf16", avg["index"])}
+                           "valu": valu_view("bf16", avg["index"]),
+                           "rows": layer.index_rows()}
     f8 = w["index_flop"] / avg["index_fp8"] / 1e12
     kernels["indexer32_fp8_kernel"] = {"ms": round(avg["index_fp8"] * 1e3, 3), "achieved": round(f8, 2),
                                        "unit": "TFLOP/s", "frac": round(f8 * 1e12 / FP8_PEAK, 4),
                                        "frac_of_bf16_peak": round(f8 * 1e12 / BF16_PEAK, 4),
                                        "traffic": measured_traffic("indexer32_fp8_kernel", wl.name),
-                                       "valu": valu_view("fp8", avg["index_fp8"])}
+                                       "valu": valu_view("fp8", avg["index_fp8"]),
+                                       "rows": layer.index_rows(fp8=True)}
 
     secondary = None
     if args.secondary and args.secondary != wl.name:

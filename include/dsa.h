@@ -153,6 +153,21 @@ int dsa_index_topk_fp8(const void* q_idx, const void* k_idx, const void* w_idx,
                        int32_t idx_dim, int32_t pool, int32_t topk, int32_t q_chunk,
                        int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Selection statistics of the last indexer launch that used `ws` (for the
+ * pipelined calls, that of their last query chunk), read after the work
+ * already enqueued on `stream` (the call synchronises the stream): the rows
+ * whose first sampled threshold kept fewer than min(topk, n_c) pools and
+ * were scored again with the wider margin (*retried_rows), and the rows that
+ * failed that too and were scored by the exact pass (*exact_rows).  This is
+ * the check that a call ran the fast path: on the pages' integer workloads
+ * no row needs the exact pass.  Sq, Sk and topk are the launch's (they fix
+ * the workspace layout); ws_bytes must be at least
+ * dsa_index_topk_ws_bytes(...) for them.  The two outputs are host pointers.
+ * Errors: DSA_INVALID_ARG (NULL or misaligned pointer), DSA_UNSUPPORTED_SHAPE,
+ * DSA_WORKSPACE_TOO_SMALL, DSA_HIP_ERROR (copy or synchronisation failed). */
+int dsa_index_topk_stats(const void* ws, size_t ws_bytes, int64_t Sq, int64_t Sk, int32_t topk,
+                         uint32_t* retried_rows, uint32_t* exact_rows, hipStream_t stream);
+
 /* Tuning override of the indexer's workgroup sub-tile, process-wide: 4, 8 or
  * 16 queries per wave (16-, 32- or 64-query sub-tiles) for every later
  * indexer launch, or 0 to let each call choose by its query count (the

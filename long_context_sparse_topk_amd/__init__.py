@@ -42,6 +42,7 @@ SIGNATURES = {
                                       _P, _P, _SZ, _P]),
     "dsa_index_topk_fp8": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32,
                                           _P, _P, _SZ, _P]),
+    "dsa_index_topk_stats": (ctypes.c_int, [_P, _SZ, _I64, _I64, _I32, _P, _P, _P]),
     "dsa_set_index_queries_per_wave": (ctypes.c_int, [_I32]),
     "dsa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
                                            _F, _P, _P, _P]),
@@ -188,6 +189,20 @@ def index_topk(q_idx, k_idx, w_idx, *, topk: int, q_chunk: int = 256, q_pos=None
             _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check("dsa_index_topk_fp8" if fp8 else "dsa_index_topk", st)
     return out
+
+
+def index_topk_stats(ws, *, Sq: int, Sk: int, topk: int) -> tuple:
+    """(retried_rows, exact_rows) of the last indexer launch on workspace `ws` (a uint8
+    device tensor passed to index_topk or index_attn_fwd): rows scored again with the
+    wider threshold margin, and rows scored by the exact pass.  Synchronises the
+    current stream."""
+    dev = ws.device
+    _want(ws, "ws", torch.uint8, 1, dev)
+    retried, exact = ctypes.c_uint32(0), ctypes.c_uint32(0)
+    st = lib().dsa_index_topk_stats(_ptr(ws), ws.numel(), Sq, Sk, topk, ctypes.addressof(retried),
+                                    ctypes.addressof(exact), _stream(dev))
+    _check("dsa_index_topk_stats", st)
+    return int(retried.value), int(exact.value)
 
 
 def set_index_queries_per_wave(queries_per_wave: int) -> None:

@@ -227,6 +227,28 @@ DSA_EXPORT int dsa_index_topk_fp8(const void* q_idx, const void* k_idx, const vo
   return hip_status(dsa::launch_index_topk_fp8(a, stream), "dsa_index_topk_fp8 launch");
 }
 
+DSA_EXPORT int dsa_index_topk_stats(const void* ws, size_t ws_bytes, int64_t Sq, int64_t Sk,
+                                    int32_t topk, uint32_t* retried_rows, uint32_t* exact_rows,
+                                    hipStream_t stream) {
+  g_err[0] = '\0';
+  int st;
+  if ((st = check_ptr(ws, "ws", 16))) return st;
+  if (!retried_rows || !exact_rows) return fail(DSA_INVALID_ARG, "retried_rows and exact_rows must not be NULL");
+  if (Sq < 1 || Sk < 1 || topk < 1 || topk > dsa::kMaxTopk)
+    return fail(DSA_UNSUPPORTED_SHAPE, "Sq=%lld Sk=%lld topk=%d", (long long)Sq, (long long)Sk, topk);
+  const dsa::IndexWorkspace L = dsa::index_ws_layout(Sq, Sk, topk);
+  if (ws_bytes < L.total) return fail(DSA_WORKSPACE_TOO_SMALL, "ws_bytes=%zu < %zu", ws_bytes, L.total);
+  uint32_t c[dsa::kIndexCounters];
+  const char* src = static_cast<const char*>(ws) + L.fb_off;
+  if ((st = hip_status(hipMemcpyAsync(c, src, sizeof(c), hipMemcpyDeviceToHost, stream),
+                       "dsa_index_topk_stats copy")))
+    return st;
+  if ((st = hip_status(hipStreamSynchronize(stream), "dsa_index_topk_stats synchronize"))) return st;
+  *exact_rows = c[0];
+  *retried_rows = c[dsa::kIndexRetryCounter];
+  return DSA_OK;
+}
+
 DSA_EXPORT int dsa_set_index_queries_per_wave(int32_t queries_per_wave) {
   g_err[0] = '\0';
   if (!dsa::set_index_queries_per_wave(queries_per_wave))

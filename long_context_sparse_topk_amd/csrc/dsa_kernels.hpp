@@ -15,8 +15,11 @@ constexpr int kMaxTopk = 2048;
 constexpr int kMaxIndexHeads = 8;       // indexer heads: one or two groups of 4 per query
 constexpr int kMaxHeads = 64;           // attention heads: groups of 16, one wave each
 // device counters at the head of the fallback region: [0] fallback-list
-// length, [1] and [2] the tile queues of the two-phase and the exact pass
-constexpr int kIndexCounters = 3;
+// length (rows the exact pass scores), [1] and [2] the tile queues of the
+// two-phase and the exact pass, [3] rows whose first threshold kept fewer
+// than min(k, n_c) pools (scored again with the wider margin)
+constexpr int kIndexCounters = 4;
+constexpr int kIndexRetryCounter = 3;
 
 // Survivors of the running threshold are staged in LDS per (wave, row block
 // of 4 queries) and moved to the per-query lists in HBM when a stage is

@@ -631,7 +631,10 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
         for (int r = 1; r < kRB; ++r) ncr = r == rb ? nc[r] : ncr;
         const int need = min(topk, __builtin_amdgcn_readlane(ncr, 16 * (q & 3)));
         if (kTwoPhase && n < need) {  // threshold estimate too high
-          if (attempt == 0) failed |= 1u << q;
+          if (attempt == 0) {
+            failed |= 1u << q;
+            if (lane == 0) atomicAdd(a.fb_count + kIndexRetryCounter, 1u);
+          }
           else if (lane == 0) a.fb_rows[atomicAdd(a.fb_count, 1u)] = (int32_t)qr;
           continue;
         }

@@ -581,7 +581,10 @@ __device__ __forceinline__ void indexer32_body(const KernelArgs& a) {
             if (8 * rb + 2 * i == (q & ~1)) ncq = __builtin_amdgcn_readlane(nc[rb][i], 32 * (q & 1));
         const int need = min(topk, ncq);
         if (kTwoPhase && n < need) {  // threshold estimate too high
-          if (attempt == 0) failed |= 1u << q;
+          if (attempt == 0) {
+            failed |= 1u << q;
+            if (lane == 0) atomicAdd(a.fb_count + kIndexRetryCounter, 1u);
+          }
           else if (lane == 0) a.fb_rows[atomicAdd(a.fb_count, 1u)] = (int32_t)qr;
           continue;
         }

@@ -102,6 +102,22 @@ def test_index_fp8_validation():
     assert L.dsa_index_topk_fp8(*a) == 3
 
 
+def test_index_stats_validation():
+    # the statistics query checks its arguments before it reads the workspace
+    L = D.lib()
+    r, e = ctypes.c_uint32(7), ctypes.c_uint32(7)
+    ra, ea = ctypes.addressof(r), ctypes.addressof(e)
+    need = D.index_topk_ws_bytes(64, 64, 8)
+    assert L.dsa_index_topk_stats(None, need, 64, 64, 8, ra, ea, None) == 1
+    assert b"ws is NULL" in L.dsa_last_error()
+    assert L.dsa_index_topk_stats(P + 4, need, 64, 64, 8, ra, ea, None) == 1
+    assert L.dsa_index_topk_stats(P, need, 64, 64, 8, None, ea, None) == 1
+    assert L.dsa_index_topk_stats(P, need, 64, 64, 0, ra, ea, None) == 2
+    assert L.dsa_index_topk_stats(P, need, 64, 64, 4096, ra, ea, None) == 2
+    assert L.dsa_index_topk_stats(P, need - 1, 64, 64, 8, ra, ea, None) == 3
+    assert (r.value, e.value) == (7, 7)   # outputs untouched on error
+
+
 def _fwd(**kw):
     a = dict(q=P, k=P, v=P, idx=P, q_pos=None, Sq=64, Sk=64, H=4, D=128, pool=4, topk=8,
              scale=0.1, out=P, lse=P)

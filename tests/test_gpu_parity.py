@@ -54,11 +54,17 @@ def _int_inputs(Sq, Sk, seed, heads=4):
             _bits(rng.integers(-3, 4, size=(Sq, heads))))
 
 
-def gpu_index(q_idx, k_idx, w_idx, topk, q_chunk=256, q_pos=None, fp8=None):
+def gpu_index(q_idx, k_idx, w_idx, topk, q_chunk=256, q_pos=None, fp8=None, stats=False):
+    """The selected ids; with stats=True also (retried rows, exact-pass rows) of the call."""
     qp = None if q_pos is None else dev_i32(q_pos)
-    idx = D.index_topk(dev_bf16(q_idx), dev_bf16(k_idx), dev_bf16(w_idx), topk=topk,
+    Sq, Sk = q_idx.shape[0], k_idx.shape[0]
+    ws = torch.empty(D.index_topk_ws_bytes(Sq, Sk, topk, idx_heads=q_idx.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+    idx = D.index_topk(dev_bf16(q_idx), dev_bf16(k_idx), dev_bf16(w_idx), topk=topk, ws=ws,
                        q_chunk=q_chunk, q_pos=qp, fp8=_INDEX_FP8[0] if fp8 is None else fp8)
     torch.cuda.synchronize()
+    if stats:
+        return idx.cpu().numpy(), D.index_topk_stats(ws, Sq=Sq, Sk=Sk, topk=topk)
     return idx.cpu().numpy()
 
 
@@ -80,9 +86,13 @@ def test_index_s4k_full(queries_per_wave):
     wl = syn.WORKLOADS["s4k"]
     d = syn.make_inputs(wl, parts=("index",))
     note(f"index s4k full qpw={queries_per_wave}")
-    got = gpu_index(d["q_idx"], d["k_idx"], d["w_idx"], wl.topk, wl.q_chunk)
+    got, (retried, exact) = gpu_index(d["q_idx"], d["k_idx"], d["w_idx"], wl.topk, wl.q_chunk, stats=True)
     ref = O.index_topk(d["q_idx"], d["k_idx"], d["w_idx"], None, wl.topk)
     assert_idx_equal("idx s4k", got, ref)
+    # the sampled thresholds hold for nearly every row (margin of 3 spreads) and the
+    # wider retry margin for all of them: the fast path ran
+    note(f"  rows retried {retried}, exact pass {exact}")
+    assert exact == 0 and retried <= wl.sq // 100
 
 
 @pytest.mark.parametrize("S,topk,heads", [(8192, 512, 4), (6000, 100, 3), (3001, 2048, 4),
@@ -205,9 +215,13 @@ def test_index_rows_at_one_position_threshold_trap(unsampled, queries_per_wave):
     w = _bits(np.ones((Sq, 4), np.float32))
     pos = np.full(Sq, Sk - 1, dtype=np.int64)
     note(f"index rows at one position, threshold trap unsampled={unsampled} qpw={queries_per_wave}")
-    got = gpu_index(q, k_idx, w, topk, q_pos=pos)
+    got, (retried, exact) = gpu_index(q, k_idx, w, topk, q_pos=pos, stats=True)
     ref = O.index_topk(q, k_idx, w, pos, topk)
     assert_idx_equal(f"idx one-position trap {unsampled}", got, ref)
+    # the first threshold (the 23rd best sampled score, that of tile 0's pool 22) keeps
+    # tile 0's 23 best pools in every row; the retry's (the 40th) keeps every unsampled
+    # pool at T = 125 and only tile 0's 40 at T = 10
+    assert retried == Sq and exact == (0 if unsampled == 125 else Sq), (retried, exact)
 
 
 def _operand_rounding(fp8):
