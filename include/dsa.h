@@ -270,8 +270,10 @@ int dsa_index_attn_fwd_fp8(const void* q_idx, const void* k_idx, const void* w_i
  * plus its bf16 rounding remainder, which keeps their fp32 precision.  dq is computed per
  * query row; dk and dv per pool of 4 keys, over the query rows whose key set
  * holds the pool, found by inverting idx in the workspace (counting per
- * chunk of rows in LDS, no global atomics).  The order in which a pool's
- * rows are summed follows LDS atomics and is not fixed from call to call.
+ * chunk of rows in LDS, no global atomics).  A pool's rows are summed in
+ * ascending row order, so dq, dk and dv are bitwise reproducible: the same
+ * inputs give the same bits on every call.  (A row that repeats an id, which
+ * the layer does not allow, contributes once to that pool's dk and dv.)
  *
  *   q, out, dout [Sq, heads, head_dim] bf16   k, v [Sk, head_dim] bf16
  *   lse [Sq, heads] fp32 (from the forward)   idx, q_pos as in the forward

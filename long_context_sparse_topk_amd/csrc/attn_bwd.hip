@@ -27,8 +27,8 @@
 //     second, so P and dS go from registers straight into it; Q and dO are
 //     read transposed from LDS (ds_read_b64_tr_b16).  Every key is written
 //     once, in bf16 (0 for keys no row attends).
-//   The order in which a pool's rows are summed follows the scatter (device
-//   atomics), so it is not fixed.
+//   A pool's rows are listed in ascending order and each wave sums a fixed
+//   block of them, so dk and dv are bitwise reproducible.
 
 #include <mutex>
 
@@ -288,13 +288,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 // holds it, as one array `list` with the rows of pool p at
 // [end[p-1], end[p]).  The rows are split into chunks and the pools into
 // slices of kInvSlice; one workgroup per (chunk, slice) counts, and later
-// places, its chunk's entries of its slice with LDS atomics, so no global
-// atomics are needed:
-//   inv_count_kernel         cnt[c][p] = entries of pool p in chunk c
-//   inv_chunk_prefix_kernel  cnt[c][p] = entries of p in chunks before c; offs[p] = total
+// places, its chunk's rows of its slice's pools in LDS, so no global atomics
+// are needed:
+//   inv_count_kernel         cnt[c][p] = rows of chunk c holding pool p
+//   inv_chunk_prefix_kernel  cnt[c][p] = rows of p in chunks before c; offs[p] = total
 //   scan kernels             offs[p] = end of p's rows (inclusive scan)
-//   inv_place_kernel         list[start(p) + cnt[c][p] + rank in chunk] = row
-// Within a (chunk, pool) the rows' order follows the LDS atomics.
+//   inv_place_kernel         list[start(p) + cnt[c][p] + rank in chunk] = row,
+//                            rows of a pool in ascending order
 struct InvArgs {
   const int32_t* idx;
   const int32_t* q_pos;
@@ -308,72 +308,6 @@ struct InvArgs {
   int32_t* offs;           // [np]
   int32_t* list;
 };
-
-// Calls f(pool - p0, row) for every entry of rows [r0, r1) whose pool lies
-// in [p0, p1).  Entry j < topk of row r (position i, nc = floor((i+1)/4)
-// complete pools) is pool idx[r][j] if 0 <= idx[r][j] < nc; entry topk is
-// the row's own incomplete pool nc if (i+1) % 4 != 0.  The workgroup's 256 threads walk
-// the entries (row, j), j = 0..topk, in row-major order, kInvUnroll entries
-// per thread at a time; the loads use in-bounds clamped indices and are
-// issued unconditionally, so that they are in flight together.
-constexpr int kInvUnroll = 8;
-
-template <bool kPos, typename F>
-__device__ __forceinline__ void for_entries(const InvArgs& a, int64_t r0, int64_t r1, int p0, int p1,
-                                            F&& f) {
-  const int per = a.topk + 1;
-  const int step_r = 256 / per, step_j = 256 % per;   // a stride of 256 entries
-  int64_t r = r0 + (int)threadIdx.x / per;
-  int j = (int)threadIdx.x % per;
-  while (r < r1) {
-    int64_t rr[kInvUnroll];
-    int jj[kInvUnroll], id[kInvUnroll], ps[kInvUnroll];
-#pragma unroll
-    for (int u = 0; u < kInvUnroll; ++u) {
-      rr[u] = r;
-      jj[u] = j;
-      const int64_t rc = r < r1 ? r : r1 - 1;
-      id[u] = a.idx[rc * a.topk + (j < a.topk ? j : a.topk - 1)];
-      ps[u] = kPos ? a.q_pos[rc] : (int)rc;
-      r += step_r;
-      j += step_j;
-      const bool wrap = j >= per;
-      j = wrap ? j - per : j;
-      r += wrap ? 1 : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kInvUnroll; ++u) {
-      if (rr[u] >= r1) continue;
-      const int pos = kPos ? (ps[u] < 0 ? 0 : (ps[u] >= a.Sk ? (int)(a.Sk - 1) : ps[u])) : ps[u];
-      const int nc = (pos + 1) >> 2;
-      int p;
-      if (jj[u] < a.topk) p = (id[u] >= 0 && id[u] < nc) ? id[u] : -1;
-      else p = ((pos + 1) & 3) ? nc : -1;
-      if (p >= p0 && p < p1) f(p - p0, rr[u]);
-    }
-  }
-}
-
-template <typename F>
-__device__ __forceinline__ void for_chunk_entries(const InvArgs& a, int64_t r0, int64_t r1, int p0,
-                                                  int p1, F&& f) {
-  if (a.q_pos) for_entries<true>(a, r0, r1, p0, p1, f);
-  else for_entries<false>(a, r0, r1, p0, p1, f);
-}
-
-__global__ __launch_bounds__(256) void inv_count_kernel(InvArgs a) {
-  __shared__ int32_t h[kInvSlice];
-  const int64_t c = blockIdx.x / a.nslices;
-  const int p0 = (int)(blockIdx.x % a.nslices) * kInvSlice;
-  const int p1 = (int)min((int64_t)p0 + kInvSlice, a.np);
-  for (int i = threadIdx.x; i < kInvSlice; i += 256) h[i] = 0;
-  __syncthreads();
-  const int64_t r0 = c * a.chunk_rows;
-  for_chunk_entries(a, r0, min(r0 + a.chunk_rows, a.Sq), p0, p1, [&](int i, int64_t) { atomicAdd(&h[i], 1); });
-  __syncthreads();
-  int32_t* dst = a.cnt + c * a.np + p0;
-  for (int i = threadIdx.x; i < p1 - p0; i += 256) dst[i] = h[i];
-}
 
 // One thread per pool: per-chunk counts -> exclusive prefix over the
 // chunks; the pool's total to offs.
@@ -401,21 +335,134 @@ __global__ __launch_bounds__(256) void inv_chunk_prefix_kernel(InvArgs a) {
   a.offs[p] = s;
 }
 
-__global__ __launch_bounds__(256) void inv_place_kernel(InvArgs a) {
-  __shared__ int32_t h[kInvSlice];
+// Both passes walk a chunk's rows in blocks of up to 32, whose entries (k + 1
+// a row) the 1024 threads read at once, kInvPer at most a thread, into
+// registers, and mark each entry's row in its pool's 32-bit mask.  A pool
+// counts the rows of its mask (a row holding a pool twice, against the
+// layer's requirement of distinct ids, counts once), and the placement gives
+// an entry the slot h[pool] + (rows of the mask before its own), so the rows of
+// a pool are listed in ascending order and the dk/dv pass sums them in an
+// order fixed by the inputs: dk and dv are bitwise reproducible.  Whichever of
+// a pool's entries first takes its mask (an exchange with 0) moves the count
+// or h[pool] on.  The barriers order LDS only: list stores need not land
+// before the next block.  (S = 2^17, k = 128: count 0.11 ms, placement 0.22,
+// as with the unordered placement by LDS atomics.)
+constexpr int kInvThreads = 1024;
+constexpr int kInvBlockRows = 32;
+constexpr int kInvPer = 8;
+
+__device__ __forceinline__ int inv_block_rows(int topk) {
+  const int r = kInvThreads * kInvPer / (topk + 1);
+  return r < 1 ? 1 : (r > kInvBlockRows ? kInvBlockRows : r);
+}
+
+// This thread's entries of rows [b0, b1) whose pool lies in [p0, p1),
+// row-major from entry threadIdx.x in strides of kInvThreads, as
+// (pool - p0) << 5 | (row - b0), else -1.  Entry j < topk of row r (position
+// i, nc = floor((i+1)/4) complete pools) is pool idx[r][j] if 0 <= idx[r][j] <
+// nc; entry topk is the row's own incomplete pool nc if (i+1) % 4 != 0.  The
+// loads use in-bounds clamped indices and are issued unconditionally, so that
+// they are in flight together.
+template <bool kPos>
+__device__ __forceinline__ void block_entries(const InvArgs& a, int64_t b0, int64_t b1, int p0, int p1,
+                                              int (&ent)[kInvPer]) {
+  const int per = a.topk + 1;
+  const int step_r = kInvThreads / per, step_j = kInvThreads % per;
+  int64_t rr[kInvPer];
+  int jj[kInvPer], id[kInvPer], ps[kInvPer];
+  int64_t r = b0 + (int)threadIdx.x / per;
+  int j = (int)threadIdx.x % per;
+#pragma unroll
+  for (int u = 0; u < kInvPer; ++u) {
+    rr[u] = r;
+    jj[u] = j;
+    const int64_t rc = r < b1 ? r : b1 - 1;
+    id[u] = a.idx[rc * a.topk + (j < a.topk ? j : a.topk - 1)];
+    ps[u] = kPos ? a.q_pos[rc] : (int)rc;
+    r += step_r;
+    j += step_j;
+    const bool wrap = j >= per;
+    j = wrap ? j - per : j;
+    r += wrap ? 1 : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kInvPer; ++u) {
+    const int pos = kPos ? (ps[u] < 0 ? 0 : (ps[u] >= a.Sk ? (int)(a.Sk - 1) : ps[u])) : ps[u];
+    const int nc = (pos + 1) >> 2;
+    int p;
+    if (jj[u] < a.topk) p = (id[u] >= 0 && id[u] < nc) ? id[u] : -1;
+    else p = ((pos + 1) & 3) ? nc : -1;
+    ent[u] = (rr[u] < b1 && p >= p0 && p < p1) ? ((p - p0) << 5) | (int)(rr[u] - b0) : -1;
+  }
+}
+
+// kPlace = false: h[pool] += rows of the chunk holding the pool; true: list the
+// rows at h[pool] onwards, ascending.
+template <bool kPos, bool kPlace>
+__device__ __forceinline__ void walk_chunk(const InvArgs& a, int32_t* h, uint32_t* msk, int64_t r0,
+                                           int64_t r1, int p0, int p1) {
+  const int rows = inv_block_rows(a.topk);
+  for (int64_t b0 = r0; b0 < r1; b0 += rows) {
+    const int64_t b1 = min(b0 + rows, r1);
+    int ent[kInvPer];
+    block_entries<kPos>(a, b0, b1, p0, p1, ent);
+#pragma unroll
+    for (int u = 0; u < kInvPer; ++u)
+      if (ent[u] >= 0) atomicOr(&msk[ent[u] >> 5], 1u << (ent[u] & 31));
+    lds_barrier();
+    if (kPlace) {
+#pragma unroll
+      for (int u = 0; u < kInvPer; ++u)
+        if (ent[u] >= 0) {
+          const int i = ent[u] >> 5, rb = ent[u] & 31;
+          a.list[h[i] + __popc(msk[i] & ((1u << rb) - 1u))] = (int32_t)(b0 + rb);
+        }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int u = 0; u < kInvPer; ++u)
+      if (ent[u] >= 0) {
+        const int i = ent[u] >> 5;
+        const uint32_t m = atomicExch(&msk[i], 0u);   // one of the pool's entries takes the mask
+        if (m != 0u) h[i] += __popc(m);
+      }
+    lds_barrier();
+  }
+}
+
+template <bool kPlace>
+__device__ __forceinline__ void inv_pass(const InvArgs& a, int32_t* h, uint32_t* msk) {
   const int64_t c = blockIdx.x / a.nslices;
   const int p0 = (int)(blockIdx.x % a.nslices) * kInvSlice;
   const int p1 = (int)min((int64_t)p0 + kInvSlice, a.np);
   const int32_t* pre = a.cnt + c * a.np;
-  for (int i = threadIdx.x; i < p1 - p0; i += 256) {
+  for (int i = threadIdx.x; i < p1 - p0; i += kInvThreads) {
     const int p = p0 + i;
-    h[i] = (p > 0 ? a.offs[p - 1] : 0) + pre[p];   // start of p's rows + earlier chunks
+    // placement: start of p's rows + earlier chunks' rows of p
+    h[i] = kPlace ? (p > 0 ? a.offs[p - 1] : 0) + pre[p] : 0;
+    msk[i] = 0u;
   }
-  __syncthreads();
+  lds_barrier();
   const int64_t r0 = c * a.chunk_rows;
-  for_chunk_entries(a, r0, min(r0 + a.chunk_rows, a.Sq), p0, p1, [&](int i, int64_t r) {
-    a.list[atomicAdd(&h[i], 1)] = (int32_t)r;
-  });
+  const int64_t r1 = min(r0 + a.chunk_rows, a.Sq);
+  if (a.q_pos) walk_chunk<true, kPlace>(a, h, msk, r0, r1, p0, p1);
+  else walk_chunk<false, kPlace>(a, h, msk, r0, r1, p0, p1);
+  if (!kPlace) {
+    int32_t* dst = a.cnt + c * a.np + p0;
+    for (int i = threadIdx.x; i < p1 - p0; i += kInvThreads) dst[i] = h[i];
+  }
+}
+
+__global__ __launch_bounds__(kInvThreads) void inv_count_kernel(InvArgs a) {
+  __shared__ int32_t h[kInvSlice];
+  __shared__ uint32_t msk[kInvSlice];
+  inv_pass<false>(a, h, msk);
+}
+
+__global__ __launch_bounds__(kInvThreads) void inv_place_kernel(InvArgs a) {
+  __shared__ int32_t h[kInvSlice];
+  __shared__ uint32_t msk[kInvSlice];
+  inv_pass<true>(a, h, msk);
 }
 
 // Inclusive scan of n counts in place, in blocks of kScanBlock: block sums,
@@ -735,12 +782,12 @@ hipError_t launch_attn_bwd(const AttnArgs& x, hipStream_t s) {
   ia.offs = offs;
   ia.list = list;
   const unsigned inv_blocks = (unsigned)(ia.chunks * ia.nslices);
-  inv_count_kernel<<<dim3(inv_blocks), dim3(256), 0, s>>>(ia);
+  inv_count_kernel<<<dim3(inv_blocks), dim3(kInvThreads), 0, s>>>(ia);
   inv_chunk_prefix_kernel<<<dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s>>>(ia);
   scan_block_sums_kernel<<<dim3((unsigned)nb), dim3(1024), 0, s>>>(offs, bsum, np);
   scan_sums_kernel<<<dim3(1), dim3(1024), 0, s>>>(bsum, nb);
   scan_apply_kernel<<<dim3((unsigned)nb), dim3(1024), 0, s>>>(offs, bsum, np);
-  inv_place_kernel<<<dim3(inv_blocks), dim3(256), 0, s>>>(ia);
+  inv_place_kernel<<<dim3(inv_blocks), dim3(kInvThreads), 0, s>>>(ia);
 
   // dq (and Delta)
   BwdArgs a;

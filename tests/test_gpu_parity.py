@@ -556,6 +556,53 @@ def test_backward_many_row_chunks_and_pool_slices():
     assert_close("chunked dk", host_f64(dk[ks]), dk_ref)
     assert_close("chunked dv", host_f64(dv[ks]), dv_ref)
     assert np.abs(dk_ref[np.isin(keys, hot_keys)]).min() > 0   # the hot keys have many rows
+    # a pool's rows are summed in ascending row order: a second call gives the same bits
+    dq2, dk2, dv2 = D.sparse_attn_bwd(tqq, tk, tv, out, dev_bf16(dout), lse, ti, q_pos=tq, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+def test_backward_repeated_ids_are_safe():
+    # The layer requires distinct ids in a row; a row that repeats one is listed once
+    # under that pool by the backward's inverse lists (their counts and slots both
+    # count rows, not entries), so no list slot is left unwritten: the call completes,
+    # the gradients are finite, keys no repeating row touches match the oracle, and a
+    # second call gives the same bits.
+    Sq, Sk, H, topk = 600, 600, 4, 16
+    rng = np.random.default_rng(29)
+    pos = np.arange(Sq)
+    idx = np.full((Sq, topk), -1, np.int32)
+    for r in range(Sq):
+        nc = (r + 1) // 4
+        m = min(topk, nc)
+        if m:
+            idx[r, :m] = np.sort(rng.choice(nc, size=m, replace=False))
+    rep = [r for r in range(16, 80) if r % 5 == 0]              # rows with 4..20 pools
+    idx[rep, 1] = idx[rep, 0]                                   # pool idx[r, 0] twice
+    q = _bits(rng.standard_normal((Sq, H, 128)).astype(np.float32))
+    k = _bits(rng.standard_normal((Sk, 128)).astype(np.float32))
+    v = _bits(rng.standard_normal((Sk, 128)).astype(np.float32))
+    dout = _bits(rng.standard_normal((Sq, H, 128)).astype(np.float32))
+    note(f"backward with {len(rep)} rows repeating an id")
+    ti = dev_i32(idx)
+    tqq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out, lse = D.sparse_attn_fwd(tqq, tk, tv, ti, scale=SCALE)
+    grads = [D.sparse_attn_bwd(tqq, tk, tv, out, dev_bf16(dout), lse, ti, scale=SCALE) for _ in range(2)]
+    torch.cuda.synchronize()
+    for a_, b_ in zip(*grads):
+        assert torch.equal(a_, b_) and bool(torch.isfinite(a_.float()).all())
+    # keys of pools that no row lists twice and that no repeating row selects
+    touched = np.zeros(Sk // 4 + 1, bool)
+    for r in rep:
+        touched[idx[r][idx[r] >= 0]] = True
+        touched[(r + 1) // 4] = True
+    clean_pools = np.nonzero(~touched[: Sk // 4])[0]
+    keys = (4 * rng.choice(clean_pools, size=12, replace=False)[:, None] + np.arange(4)).ravel()
+    _, dk_ref, dv_ref = O.sparse_attn_bwd(q, k, v, dout, idx, pos, SCALE, rows=np.array([Sq - 1]),
+                                          key_rows=keys)
+    dk1, dv1 = grads[0][1], grads[0][2]
+    assert_close("dk, clean keys", host_f64(dk1[torch.from_numpy(keys).cuda()]), dk_ref)
+    assert_close("dv, clean keys", host_f64(dv1[torch.from_numpy(keys).cuda()]), dv_ref)
 
 
 @pytest.mark.parametrize("name", ["s128k", "zigzag4"])
