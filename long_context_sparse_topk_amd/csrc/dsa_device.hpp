@@ -132,7 +132,8 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // row; after the first k of these four steps a lane holds the combination of
 // 2^k lanes of its row.  row_shr:n reads the lane n before (0 before the row
 // start, with bound_ctrl); row_bcast:15 / :31 read lane 15 of the row before /
-// lane 31, in the rows that row_mask enables.
+// lane 31, in the rows that row_mask enables.  The helpers below read other
+// lanes' values, so they are called with all 64 lanes of the wave active.
 constexpr int kDppQuadSwap1 = 0xB1;
 constexpr int kDppQuadSwap2 = 0x4E;
 constexpr int kDppRowHalfMirror = 0x141;
