@@ -55,13 +55,18 @@ struct IndexWorkspace {
   size_t kpool_off, cand_off, fb_off, total;
 };
 
+// pooled keys | counters (256 B), fallback rows | candidate lists.  The pooled
+// keys and the counters sit at offsets that depend on Sk only, so the query
+// chunks of a pipelined call (each laid out for its own rows in the call's
+// workspace) share them, and the counters of the last chunk are where
+// dsa_index_topk_stats reads them for the whole call's shape.
 inline IndexWorkspace index_ws_layout(int64_t Sq, int64_t Sk, int topk) {
   IndexWorkspace w;
   const size_t cand = (size_t)index_slots(Sq) * kIndexQueryTile * index_candidate_cap(topk);
   w.kpool_off = 0;
-  w.cand_off = align256((size_t)index_padded_pools(Sk) * 64 * 2);
-  w.fb_off = w.cand_off + align256(cand * 8);          // counters (256 B), fallback rows
-  w.total = w.fb_off + 256 + align256((size_t)Sq * 4);
+  w.fb_off = align256((size_t)index_padded_pools(Sk) * 64 * 2);
+  w.cand_off = w.fb_off + 256 + align256((size_t)Sq * 4);
+  w.total = w.cand_off + align256(cand * 8);
   return w;
 }
 

@@ -698,11 +698,24 @@ def test_pipelined_exact_fallback(fp8):
     v = _bits(rng.standard_normal((S, 128)).astype(np.float32))
     note(f"pipelined threshold trap, 2 chunks, fp8={fp8}")
     dqi, dki, dwi, dq, dk, dv = (dev_bf16(x) for x in (qi, k_idx, wi, q, k, v))
-    idx_p, out_p, lse_p = D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, scale=SCALE, fp8=fp8)
-    idx_s = D.index_topk(dqi, dki, dwi, topk=topk, fp8=fp8)
+    ws_p, ws_s = (torch.empty(D.index_topk_ws_bytes(S, S, topk), dtype=torch.uint8, device="cuda")
+                  for _ in range(2))
+    idx_p, out_p, lse_p = D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, scale=SCALE, fp8=fp8,
+                                           ws=ws_p)
+    idx_s = D.index_topk(dqi, dki, dwi, topk=topk, fp8=fp8, ws=ws_s)
     out_s, lse_s = D.sparse_attn_fwd(dq, dk, dv, idx_s, scale=SCALE)
     torch.cuda.synchronize()
     assert torch.equal(idx_p, idx_s) and torch.equal(out_p, out_s) and torch.equal(lse_p, lse_s)
+    # every row with a usable sample fails its first threshold here, and all but a few
+    # short rows (whose wider-margin rank exceeds the sample) the retry too: the separate
+    # call sends nearly all S rows to the exact pass, and the pipelined call's counters,
+    # those of its last chunk (about 39% of the rows, all long), every row of that chunk
+    retried_s, exact_s = D.index_topk_stats(ws_s, Sq=S, Sk=S, topk=topk)
+    retried_p, exact_p = D.index_topk_stats(ws_p, Sq=S, Sk=S, topk=topk)
+    note(f"  separate: retried {retried_s}, exact {exact_s}; pipelined last chunk: {retried_p}, {exact_p}")
+    last = S - int(round(S * np.sqrt(0.75 / 2) / 64)) * 64
+    assert exact_s > 0.99 * S and exact_s <= retried_s < exact_s + 0.01 * S
+    assert retried_p == exact_p == last
     rows = sample_rows(S, topk, None, n_random=16)
     ref = O.index_topk(qi, k_idx, wi, None, topk, rows=rows)
     assert_idx_equal("pipelined trap idx", idx_p[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, rows)
