@@ -159,8 +159,10 @@ int dsa_index_topk_fp8(const void* q_idx, const void* k_idx, const void* w_idx,
  * whose first sampled threshold kept fewer than min(topk, n_c) pools and
  * were scored again with the wider margin (*retried_rows), and the rows that
  * failed that too and were scored by the exact pass (*exact_rows).  This is
- * the check that a call ran the fast path: on the pages' integer workloads
- * no row needs the exact pass.  Sq, Sk and topk are the launch's (they fix
+ * the check that a call ran the fast path (the lessons paragraph of "How Lila
+ * Sciences and Anyscale Scaled GLM-5.3-Flash Training..." asks to confirm that
+ * every layer runs the kernel one expects): on the integer workloads no row
+ * needs the exact pass.  Sq, Sk and topk are the launch's (they fix
  * the workspace layout); ws_bytes must be at least
  * dsa_index_topk_ws_bytes(...) for them.  The two outputs are host pointers.
  * Errors: DSA_INVALID_ARG (NULL or misaligned pointer), DSA_UNSUPPORTED_SHAPE,
