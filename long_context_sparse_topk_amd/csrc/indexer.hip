@@ -90,9 +90,9 @@ constexpr int kSampleKeep = 8;   // sampled scores kept per lane and query
 // Survivor-stage entries per (wave, row block) and key-ring buffers, per
 // sub-tile.  The 32-query sub-tile (kRB = 2) is sized for four workgroups a CU
 // (four waves a SIMD): 128 registers and 40 KB of LDS, from a two-buffer key
-// ring (16 KB, loads one tile ahead) and 376-entry stages (24 KB), with each
-// column block's products and epilogue done before the next block's operands
-// are read.  Measured at S = 2^20 (same ids): 77.6 ms against 85.9 ms at three
+// ring (16 KB, loads one tile ahead) and 376-entry stages (24 KB), with the
+// products of at most two column blocks live at a time.  Measured at S = 2^20
+// (same ids, one block at a time then): 77.6 ms against 85.9 ms at three
 // workgroups a CU (three-buffer ring, 440-entry stages, all four blocks'
 // products first, 157 registers); S = 2^17: 2.01 against 2.28 ms.  (The
 // three-buffer ring issues loads two tiles ahead, but the barrier's release
@@ -330,13 +330,20 @@ __global__ __launch_bounds__(kThreads, kRB == 2 ? 4 : 2) void indexer_topk_kerne
             }
         };
         if constexpr (kRB == 2) {
-          // one column block at a time: fewer live registers, four waves a SIMD
+          // two column blocks' products live at a time (four waves a SIMD fit
+          // in 128 registers): block cb + 1's products are issued before
+          // block cb's epilogue, so the matrix core works on them while this
+          // wave's VALU clamps and sums block cb (S = 2^20: 75.7-78.9 ms
+          // against 77.2-80.7 with one block at a time, same ids)
+          f32x4_t x0[kRB][kHG], x1[kRB][kHG];
+          products(0, x0);
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            f32x4_t x[kRB][kHG];
-            products(cb, x);
+            f32x4_t (&cur)[kRB][kHG] = (cb & 1) ? x1 : x0;
+            f32x4_t (&nxt)[kRB][kHG] = (cb & 1) ? x0 : x1;
+            if (cb < 3) products(cb + 1, nxt);
 #pragma unroll
-            for (int rb = 0; rb < kRB; ++rb) sc[rb][cb] = head_sum(x[rb], rb);
+            for (int rb = 0; rb < kRB; ++rb) sc[rb][cb] = head_sum(cur[rb], rb);
           }
         } else {
           // every block's products first, then the epilogues (one or two waves a SIMD)
