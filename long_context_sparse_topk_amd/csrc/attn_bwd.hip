@@ -29,6 +29,15 @@
 //     once, in bf16 (0 for keys no row attends).
 //   A pool's rows are listed in ascending order and each wave sums a fixed
 //   block of them, so dk and dv are bitwise reproducible.
+//
+// Rows staged through LDS (K in the dq pass, Q and dO in the dk/dv pass) are
+// gathered 16 lanes per 256-byte row, so that the four lanes of a quad read
+// one contiguous segment, and the MFMA operands are read back from LDS: a
+// gather whose quads read four different rows (the MFMA operand order) stays
+// below ~9.5 TB/s even from L2.  S = 2^17 backward 9.3-9.4 -> 8.5-8.8 ms,
+// zig-zag share 5.2-5.4 -> 4.8-5.0 ms, same gradients.  V of the dq pass, an
+// MFMA operand only, stays in the operand order (staging it too gained
+// nothing).
 
 #include <mutex>
 
@@ -140,7 +149,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   // past the last tile read the query's own key row.  Slot info is double
   // buffered in LDS.
   struct Buf {
-    bf16x8_t KA[2][4], VA[2][4];
+    u32x4_t KR[8];
+    bf16x8_t VA[2][4];
   };
   // slot ids of tile t: lane j (mod 8) reads id 8t + j, clamped into the row
   auto load_ids = [&](int t) -> int {
@@ -174,32 +184,34 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       const int2 in = info[4 * kb + (c16 >> 2)];
       const int off = c16 & 3;
       const int64_t key = off < in.y ? in.x + off : pos;
-      const uint16_t* ksrc = a.k + key * kD + 8 * g;
       const uint16_t* vsrc = a.v + key * kD + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        B.KA[kb][ks] = load_bf16x8(ksrc + 32 * ks);
-        B.VA[kb][ks] = load_bf16x8(vsrc + 32 * ks);
-      }
+      for (int ks = 0; ks < 4; ++ks) B.VA[kb][ks] = load_bf16x8(vsrc + 32 * ks);
+    }
+    // K rows (staged through LDS): 16 lanes per 256-byte row, slot j, key offset g
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int2 in = info[j];
+      const int64_t key = g < in.y ? in.x + g : pos;
+      B.KR[j] = *reinterpret_cast<const u32x4_t*>(a.k + key * kD + 8 * c16);
     }
   };
   auto compute = [&](int t, const Buf& B) {
     const int2* info = lds_info[wave][t & 1];
-    // K rows also go to LDS, to be read transposed for dQ
+    // K rows go to LDS: read back as the A operand of S, and transposed for dQ
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      uint16_t* kdst = kt + (16 * kb + c16) * kKStride + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<u32x4_t*>(kdst + 32 * ks) = __builtin_bit_cast(u32x4_t, B.KA[kb][ks]);
-    }
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4_t*>(kt + (4 * j + g) * kKStride + 8 * c16) = B.KR[j];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     float ds[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* ksrc = kt + (16 * kb + c16) * kKStride + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        s = mfma32(B.KA[kb][ks], QB[ks], s);
+        s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4_t*>(ksrc + 32 * ks)), QB[ks], s);
         dp = mfma32(B.VA[kb][ks], DB[ks], dp);
       }
       const int nv = info[4 * kb + g].y;
@@ -643,14 +655,16 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
 
   // rows lst (lane j: entry j of the chunk), step s of the chunk, chunk length m
   auto load_step = [&](int lst, int s, int m, KvStep& o) {
-    int ja, ha;
-    const bool va = pair_of(s, c16, ja, ha) && ja < m;  // A lanes: pair c16
-    const int64_t ra = __shfl(lst, ja & 63, kWave);
-    const int64_t aoff = ((va ? ra : 0) * H + (va ? ha : 0)) * kD + 8 * g;
+    // Q and dO rows, 16 lanes per 256-byte (row, head) row: load j brings
+    // pair 4j + g, 16-byte chunk c16
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      o.q[ks] = va ? *reinterpret_cast<const u32x4_t*>(a.q + aoff + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
-      o.d[ks] = va ? *reinterpret_cast<const u32x4_t*>(a.dout + aoff + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 4; ++j) {
+      int jp, hp;
+      const bool vp = pair_of(s, 4 * j + g, jp, hp) && jp < m;
+      const int64_t rp = __shfl(lst, jp & 63, kWave);
+      const int64_t poff = ((vp ? rp : 0) * H + (vp ? hp : 0)) * kD + 8 * c16;
+      o.q[j] = vp ? *reinterpret_cast<const u32x4_t*>(a.q + poff) : u32x4_t{0u, 0u, 0u, 0u};
+      o.d[j] = vp ? *reinterpret_cast<const u32x4_t*>(a.dout + poff) : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {                        // D lanes: pairs 4g + i
@@ -670,15 +684,20 @@ __global__ __launch_bounds__(kKvWaves * kWave, 2) void attn_bwd_dkdv_kernel(KvAr
     for (int s = 0; s < nsteps; ++s) {
       if (s + 1 < nsteps) load_step(lst, s + 1, m, nxt);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        *reinterpret_cast<u32x4_t*>(tq + c16 * kTStride + 8 * g + 32 * ks) = cur.q[ks];
-        *reinterpret_cast<u32x4_t*>(tdo + c16 * kTStride + 8 * g + 32 * ks) = cur.d[ks];
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<u32x4_t*>(tq + (4 * j + g) * kTStride + 8 * c16) = cur.q[j];
+        *reinterpret_cast<u32x4_t*>(tdo + (4 * j + g) * kTStride + 8 * c16) = cur.d[j];
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // A operands from the tiles: pair c16, dims 8g + 32ks
       f32x4_t sv = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        sv = mfma32(as_bf16x8(cur.q[ks]), KB[ks], sv);
-        dp = mfma32(as_bf16x8(cur.d[ks]), VB[ks], dp);
+        const u32x4_t qa = *reinterpret_cast<const u32x4_t*>(tq + c16 * kTStride + 8 * g + 32 * ks);
+        const u32x4_t da = *reinterpret_cast<const u32x4_t*>(tdo + c16 * kTStride + 8 * g + 32 * ks);
+        sv = mfma32(as_bf16x8(qa), KB[ks], sv);
+        dp = mfma32(as_bf16x8(da), VB[ks], dp);
       }
       // lane holds S[(row, head) 4g+i][key c16]
       float pv[4], dsv[4];

@@ -17,6 +17,16 @@
 // The K rows are loaded straight into MFMA A-operand registers; V goes
 // through LDS to be read transposed.  With keys as M and heads as N, each lane
 // owns one head, so the online-softmax rescale is a per-lane scalar.
+//
+// Gather lane order: in the MFMA operand order the four lanes of a quad read
+// four different rows, and such a gather stays below ~9.5 TB/s even when
+// every row hits in L2; with 16 lanes reading one 256-byte row (a quad reads
+// one contiguous 64-byte segment) the same gather reaches ~26 TB/s from L2
+// and ~8% more from beyond it (a probe gathering random rows of 0.5 MB to
+// 256 MB tables).  V, which is staged through LDS anyway, is loaded in the
+// row-contiguous order: S = 2^20 141.6 -> 139.4 ms, S = 2^15 3.6 -> 2.6 ms,
+// S = 2^12 0.147 -> 0.105 ms, same outputs.  K read through LDS in that
+// order as well helped less than the extra LDS round trip cost at S = 2^20.
 
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
@@ -117,7 +127,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   // slots.  Slot info is double buffered in LDS.
   struct Buf {
     bf16x8_t KA[2][4];
-    u32x4_t VR[2][4];
+    u32x4_t VR[8];
   };
   // slot ids of tile t: lane j (mod 8) reads id 8t + j, clamped into the row
   // so the load is unconditional (ids at or past np are not used)
@@ -155,22 +165,23 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
       const int off = c16 & 3;
       const int64_t key = off < in.y ? in.x + off : pos;
       const uint16_t* ks_src = a.k + key * kD + 8 * g;
-      const uint16_t* vs_src = a.v + key * kD + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        B.KA[kb][ks] = load_bf16x8(ks_src + 32 * ks);
-        B.VR[kb][ks] = *reinterpret_cast<const u32x4_t*>(vs_src + 32 * ks);
-      }
+      for (int ks = 0; ks < 4; ++ks) B.KA[kb][ks] = load_bf16x8(ks_src + 32 * ks);
+    }
+    // V rows: 16 lanes per 256-byte row (slot j, key offset g), so that the
+    // lanes of a quad read one contiguous segment
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int2 in = info[j];
+      const int64_t key = g < in.y ? in.x + g : pos;
+      B.VR[j] = *reinterpret_cast<const u32x4_t*>(a.v + key * kD + 8 * c16);
     }
   };
   auto compute = [&](int t, const Buf& B) {
     const int2* info = lds_info[wave][kPrefetch ? (t & 1) : 0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      uint16_t* vdst = vt + (16 * kb + c16) * kVStride + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4_t*>(vdst + 32 * ks) = B.VR[kb][ks];
-    }
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4_t*>(vt + (4 * j + g) * kVStride + 8 * c16) = B.VR[j];
     f32x4_t S[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
