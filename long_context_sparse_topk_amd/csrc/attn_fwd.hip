@@ -37,6 +37,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kRows = 4;        // query rows (waves) per workgroup
 constexpr int kVStride = 136;   // LDS row stride (elements) of the V tile
+constexpr float kLazyLog2 = 8.f;  // log2 of the largest P before the reference max moves
 
 struct FwdArgs {
   const uint16_t* q;
@@ -205,20 +206,32 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float mnew = fmaxf(m2, tmax);
-    const float ms = mnew == NEG_INF ? 0.f : mnew;
-    const float alpha = exp2f(m2 - ms);
+    // The reference m2 of a head moves only when a logit exceeds it by more
+    // than kLazyLog2 (or on its first finite logit), so P <= 2^kLazyLog2 and
+    // the rescale of O and the sum, skipped by the whole wave when no head
+    // moves, runs a few times per row instead of on most tiles (S = 2^15
+    // 2.77 -> 2.62-2.66 ms, S = 2^17 3.52-3.65 -> 3.38-3.51 ms; outputs
+    // within one bf16 ulp of the rescale on every new maximum).  The
+    // exponentials are bare v_exp_f32: a P below 2^-126 of the reference
+    // flushes to zero.
+    const bool move = tmax > m2 + kLazyLog2;
+    if (ballot(move)) {
+      const float mref = move ? tmax : m2;
+      const float alpha = mref == m2 ? 1.f : __builtin_amdgcn_exp2f(m2 - mref);  // 0 from -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+      m2 = mref;
+    }
+    const float ms = m2 == NEG_INF ? 0.f : m2;
     float p[8];
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = exp2f(lg[j] - ms);
+      p[j] = __builtin_amdgcn_exp2f(lg[j] - ms);
       psum += p[j];
     }
-    lsum = lsum * alpha + psum;
-    m2 = mnew;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    lsum += psum;
 
     u32x4_t pb;
     pb[0] = pack_bf16x2(p[0], p[1]);
