@@ -376,12 +376,17 @@ def main():
                                    "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     dom = max(kern, key=lambda n: kern[n]["s"])
     dk = kern[dom]
+    traffic = measured_traffic(dom, wl.name)
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": round(dk["achieved"], 2), "peak": dk["peak"],
                 "unit": dk["unit"], "frac": round(dk["achieved"] / dk["peak"], 4),
-                "traffic": measured_traffic(dom, wl.name), "ms_per_launch": round(dk["s"] * 1e3, 3),
+                "traffic": traffic, "ms_per_launch": round(dk["s"] * 1e3, 3),
                 # inside the pipelined step the kernels share the CUs, so the launch durations come
                 # from the pass of separate calls right after the timed steps
                 "launches": "separate calls after the timed steps"}
+    if traffic is not None and dk["bound"] == "hbm":
+        # the measured bytes beyond L2 (the 256 MB MALL serves part of them) per second, against
+        # the HBM peak: the algorithmic rate above counts every gathered row, cached or not
+        roofline["traffic_frac"] = round(traffic / dk["s"] / HBM_PEAK, 4)
     kernels = {n: {"ms": round(v["s"] * 1e3, 3), "achieved": round(v["achieved"], 2), "unit": v["unit"],
                    "frac": round(v["achieved"] / v["peak"], 4)} for n, v in kern.items()}
     # the indexer beside the dominant kernel (bf16 MFMA-bound), and the fp8 variant (opt-in,
