@@ -38,6 +38,13 @@ constexpr int kD = 128;
 constexpr int kRows = 4;        // query rows (waves) per workgroup
 constexpr int kVStride = 136;   // LDS row stride (elements) of the V tile
 constexpr float kLazyLog2 = 8.f;  // log2 of the largest P before the reference max moves
+// Up to this many keys (K and V together at most 64 MiB) the forward stages
+// K through LDS too: S = 2^15 2.71 -> 2.31-2.33 ms, S = 2^12 0.102-0.105 ->
+// 0.093-0.095, S = 2^17 3.50-3.57 -> 3.40-3.41; at 2^18 keys (the zig-zag
+// share) it changes nothing, and at S = 2^20, where the fabric below L2
+// binds, it costs about 1% (139.0 against 137.9-138.2 ms), so larger key sets
+// load K straight into MFMA registers.
+constexpr int64_t kStagedMaxKeys = int64_t(1) << 17;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -71,9 +78,12 @@ __device__ __forceinline__ int2 slot_info(const int32_t* irow, int ps, int np, i
   return make_int2(base, nv);
 }
 
-template <bool kPrefetch>
+// kKStaged: K rows go through LDS as well (gathered 16 lanes per row, read
+// back as the MFMA operand), for key sets the caches hold (kStagedMaxKeys).
+template <bool kPrefetch, bool kKStaged>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   __shared__ __align__(16) uint16_t lds_v[kRows][32 * kVStride];
+  __shared__ __align__(16) uint16_t lds_k[kRows][kKStaged ? 32 * kVStride : 8];
   __shared__ int2 lds_info[kRows][kPrefetch ? 2 : 1][8];  // slot info, double buffered when prefetching
 
   const int lane = lane_id();
@@ -117,6 +127,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m2 = NEG_INF, lsum = 0.f;
   uint16_t* vt = lds_v[wave];
+  uint16_t* kt = lds_k[wave];
 
   // Two schedules.  kPrefetch (the kernel has the GPU to itself): the K/V
   // rows of the next tile are in flight while a tile is computed, with two
@@ -127,7 +138,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   // it fits beside an indexer wave on a SIMD and leaves that wave the issue
   // slots.  Slot info is double buffered in LDS.
   struct Buf {
-    bf16x8_t KA[2][4];
+    bf16x8_t KA[kKStaged ? 1 : 2][4];
+    u32x4_t KR[kKStaged ? 8 : 1];
     u32x4_t VR[8];
   };
   // slot ids of tile t: lane j (mod 8) reads id 8t + j, clamped into the row
@@ -160,35 +172,50 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
     const int2* info = lds_info[wave][kPrefetch ? (t & 1) : 0];
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    if constexpr (!kKStaged) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int2 in = info[4 * kb + (c16 >> 2)];
-      const int off = c16 & 3;
-      const int64_t key = off < in.y ? in.x + off : pos;
-      const uint16_t* ks_src = a.k + key * kD + 8 * g;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int2 in = info[4 * kb + (c16 >> 2)];
+        const int off = c16 & 3;
+        const int64_t key = off < in.y ? in.x + off : pos;
+        const uint16_t* ks_src = a.k + key * kD + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) B.KA[kb][ks] = load_bf16x8(ks_src + 32 * ks);
+        for (int ks = 0; ks < 4; ++ks) B.KA[kb][ks] = load_bf16x8(ks_src + 32 * ks);
+      }
     }
-    // V rows: 16 lanes per 256-byte row (slot j, key offset g), so that the
-    // lanes of a quad read one contiguous segment
+    // V (and staged K) rows: 16 lanes per 256-byte row (slot j, key offset
+    // g), so that the lanes of a quad read one contiguous segment
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int2 in = info[j];
       const int64_t key = g < in.y ? in.x + g : pos;
+      if constexpr (kKStaged) B.KR[j] = *reinterpret_cast<const u32x4_t*>(a.k + key * kD + 8 * c16);
       B.VR[j] = *reinterpret_cast<const u32x4_t*>(a.v + key * kD + 8 * c16);
     }
   };
   auto compute = [&](int t, const Buf& B) {
     const int2* info = lds_info[wave][kPrefetch ? (t & 1) : 0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (kKStaged) *reinterpret_cast<u32x4_t*>(kt + (4 * j + g) * kVStride + 8 * c16) = B.KR[j];
       *reinterpret_cast<u32x4_t*>(vt + (4 * j + g) * kVStride + 8 * c16) = B.VR[j];
+    }
+    if constexpr (kKStaged) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
     f32x4_t S[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       S[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* ksrc = kt + (16 * kb + c16) * kVStride + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) S[kb] = mfma32(B.KA[kb][ks], QB[ks], S[kb]);
+      for (int ks = 0; ks < 4; ++ks) {
+        if constexpr (kKStaged)
+          S[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4_t*>(ksrc + 32 * ks)), QB[ks], S[kb]);
+        else
+          S[kb] = mfma32(B.KA[kb][ks], QB[ks], S[kb]);
+      }
     }
 
     // lane holds keys 16*kb + 4*g + rr (pool slot 4*kb + g, offset rr) of head c16
@@ -334,9 +361,11 @@ hipError_t launch_attn_fwd(const AttnArgs& x, hipStream_t s) {
   a.lse = x.lse_out;
   const int64_t blocks = (x.Sq * a.HG + kRows - 1) / kRows;
   if (x.fwd_shared)
-    attn_fwd_kernel<false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+    attn_fwd_kernel<false, false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+  else if (x.Sk <= kStagedMaxKeys)
+    attn_fwd_kernel<true, true><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
   else
-    attn_fwd_kernel<true><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+    attn_fwd_kernel<true, false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
   return hipGetLastError();
 }
 
