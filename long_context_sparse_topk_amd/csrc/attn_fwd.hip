@@ -80,8 +80,19 @@ __device__ __forceinline__ int2 slot_info(const int32_t* irow, int ps, int np, i
 
 // kKStaged: K rows go through LDS as well (gathered 16 lanes per row, read
 // back as the MFMA operand), for key sets the caches hold (kStagedMaxKeys).
-template <bool kPrefetch, bool kKStaged>
+// kHold (shared schedule only): the kernel claims 272 of a SIMD's 512
+// registers, so at most one forward wave sits on a SIMD and a 240-register
+// indexer wave always finds room beside it.  Without the hold the shared
+// forward (184 registers) puts two waves on SIMDs the indexer has not reached
+// yet, and the indexer's workgroups of a new chunk wait for them: pipelined
+// S = 2^20 step 186.6-186.8 ms with the hold against 189.1-189.7 without.
+// The fp8 indexer's shared chunks keep two 128-register workgroups a CU,
+// which a held forward wave would not fit beside (215 against 178 ms), so
+// they use the unheld instance.
+template <bool kPrefetch, bool kKStaged, bool kHold>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
+  // an empty asm that clobbers v231 makes the allocation 232 VGPRs (+ 40 AGPRs)
+  if constexpr (kHold) asm volatile("" ::: "v231");
   __shared__ __align__(16) uint16_t lds_v[kRows][32 * kVStride];
   __shared__ __align__(16) uint16_t lds_k[kRows][kKStaged ? 32 * kVStride : 8];
   __shared__ int2 lds_info[kRows][kPrefetch ? 2 : 1][8];  // slot info, double buffered when prefetching
@@ -360,12 +371,14 @@ hipError_t launch_attn_fwd(const AttnArgs& x, hipStream_t s) {
   a.out = x.out;
   a.lse = x.lse_out;
   const int64_t blocks = (x.Sq * a.HG + kRows - 1) / kRows;
-  if (x.fwd_shared)
-    attn_fwd_kernel<false, false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+  if (x.fwd_shared && x.fwd_hold)
+    attn_fwd_kernel<false, false, true><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+  else if (x.fwd_shared)
+    attn_fwd_kernel<false, false, false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
   else if (x.Sk <= kStagedMaxKeys)
-    attn_fwd_kernel<true, true><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+    attn_fwd_kernel<true, true, false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
   else
-    attn_fwd_kernel<true, false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
+    attn_fwd_kernel<true, false, false><<<dim3((unsigned)blocks), dim3(kRows * kWave), 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -395,6 +395,7 @@ int index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx, cons
     fa.out = oo + r0 * heads * head_dim;
     fa.lse_out = lse + r0 * heads;
     fa.fwd_shared = n > 1 && c + 1 < n;   // the last chunk's forward runs after the indexer
+    fa.fwd_hold = fa.fwd_shared && !fp8;  // beside the 64-query bf16 sub-tile (240 registers a wave)
     note(dsa::launch_attn_fwd(fa, fs));
   }
   if (n > 1) {

@@ -112,6 +112,7 @@ struct AttnArgs {
   uint16_t* dv;           // bwd only
   void* ws;               // bwd only
   bool fwd_shared;        // fwd: the launch shares the CUs with the indexer (lean schedule)
+  bool fwd_hold;          // fwd, shared: at most one forward wave a SIMD (beside a bf16 indexer wave)
 };
 
 // Backward workspace: per (row, head) a 16-byte record (LSE in log2 units,
