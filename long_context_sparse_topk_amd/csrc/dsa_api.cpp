@@ -90,11 +90,14 @@ int check_index_shape(int64_t Sq, int64_t Sk, int32_t idx_heads, int32_t idx_dim
 // Query chunks of the pipelined indexer + forward: about one per 2^17 query
 // rows, at most kPipeChunks.  Row r at position r costs the indexer about r
 // pool scores, so the rows below b cost a share (b / Sq)^2 of its work.  The
-// first chunk's indexer overlaps nothing and gets 3/4 of an equal share,
-// w_1 = 3 / (4n); the others split the rest evenly, w_c = w_1 + (1 - w_1)(c - 1)
-// / (n - 1); boundary c sits at Sq * sqrt(w_c), on a multiple of the indexer's
-// 64-query tile.  (At S = 2^20, six chunks: 195.8 ms against 197.2 with equal
-// shares; a first share of 0.09, 0.06 or 0.04 was slower, 203-209 ms.)
+// first chunk's indexer overlaps nothing and gets a share w_1 = f / n of it
+// (f of an equal share); the others split the rest evenly, w_c = w_1 + (1 -
+// w_1)(c - 1) / (n - 1); boundary c sits at Sq * sqrt(w_c), on a multiple of
+// the indexer's 64-query tile.  With the bf16 indexer the chain of indexer
+// chunks is the longer one, and its first chunk runs at the full-GPU rate, so
+// f = 1.05 (S = 2^20, six chunks: 180.2-181.1 ms for f in 1.0-1.1 against
+// 184.4 at 0.95 and 185.7 at 0.75, and 184-186 from 1.3 up); with the fp8
+// indexer f = 0.75 (176.9 ms against 178.0 at 1.0).
 constexpr int kPipeChunks = 6;
 constexpr int64_t kPipeRowsPerChunk = (int64_t)1 << 17;
 
@@ -103,10 +106,10 @@ int pipe_chunks(int64_t Sq) {
   return n < 1 ? 1 : (n > kPipeChunks ? kPipeChunks : (int)n);
 }
 
-int64_t pipe_bound(int64_t Sq, int c, int n) {
+int64_t pipe_bound(int64_t Sq, int c, int n, double first_share) {
   if (c <= 0) return 0;
   if (c >= n) return Sq;
-  const double w1 = 0.75 / (double)n;
+  const double w1 = first_share / (double)n;
   const double w = w1 + (1.0 - w1) * (double)(c - 1) / (double)(n - 1);
   const double x = (double)Sq * std::sqrt(w);
   int64_t b = (int64_t)std::llround(x / dsa::kIndexQueryTile) * dsa::kIndexQueryTile;
@@ -355,7 +358,8 @@ int index_attn_fwd(const void* q_idx, const void* k_idx, const void* w_idx, cons
   auto* oo = static_cast<uint16_t*>(out);
   bool pooled = false;  // the workspace holds the pooled keys (chunks run in order on `stream`)
   for (int c = 0; c < n && err == hipSuccess; ++c) {
-    const int64_t r0 = pipe_bound(Sq, c, n), r1 = pipe_bound(Sq, c + 1, n);
+    const double f = fp8 ? 0.75 : 1.05;
+    const int64_t r0 = pipe_bound(Sq, c, n, f), r1 = pipe_bound(Sq, c + 1, n, f);
     if (r1 <= r0) continue;
     dsa::IndexArgs ia{};
     ia.q_idx = qi + r0 * idx_heads * idx_dim;

@@ -670,7 +670,9 @@ def test_pipelined_equals_separate_calls(Sq, Sk, H, topk, zigzag, same_stream, f
     assert torch.equal(out_p, out_s), "pipelined out differs from dsa_sparse_attn_fwd"
     assert torch.equal(lse_p, lse_s), "pipelined lse differs from dsa_sparse_attn_fwd"
     # and the oracle on sampled rows, chunk boundaries included
-    bounds = [int(round(Sq * np.sqrt(0.75 / 2) / 64)) * 64]   # the one inner boundary of 2 chunks
+    # the one inner boundary of 2 chunks: the first takes f/2 of the indexer work
+    # (f = 0.75 with the fp8 indexer, 1.05 with the bf16 one)
+    bounds = [int(round(Sq * np.sqrt((0.75 if fp8 else 1.05) / 2) / 64)) * 64]
     rows = np.unique(np.concatenate([sample_rows(Sq, topk, pos, n_random=24),
                                      [b + d for b in bounds for d in (-1, 0, 1) if 0 <= b + d < Sq]]))
     ref_idx = O.index_topk(qi, ki, wi, pos, topk, rows=rows)
@@ -709,11 +711,14 @@ def test_pipelined_exact_fallback(fp8):
     # every row with a usable sample fails its first threshold here, and all but a few
     # short rows (whose wider-margin rank exceeds the sample) the retry too: the separate
     # call sends nearly all S rows to the exact pass, and the pipelined call's counters,
-    # those of its last chunk (about 39% of the rows, all long), every row of that chunk
+    # those of its last chunk (all long rows), every row of that chunk.  The first of the
+    # two chunks takes a share f/2 of the indexer work (f = 1.05 with the bf16 indexer,
+    # 0.75 with the fp8 one), so the second holds the rows past S * sqrt(f / 2)
     retried_s, exact_s = D.index_topk_stats(ws_s, Sq=S, Sk=S, topk=topk)
     retried_p, exact_p = D.index_topk_stats(ws_p, Sq=S, Sk=S, topk=topk)
     note(f"  separate: retried {retried_s}, exact {exact_s}; pipelined last chunk: {retried_p}, {exact_p}")
-    last = S - int(round(S * np.sqrt(0.75 / 2) / 64)) * 64
+    f = 0.75 if fp8 else 1.05
+    last = S - int(round(S * np.sqrt(f / 2) / 64)) * 64
     assert exact_s > 0.99 * S and exact_s <= retried_s < exact_s + 0.01 * S
     assert retried_p == exact_p == last
     rows = sample_rows(S, topk, None, n_random=16)
