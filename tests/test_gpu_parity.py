@@ -726,6 +726,38 @@ def test_pipelined_exact_fallback(fp8):
     assert_idx_equal("pipelined trap idx", idx_p[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, rows)
 
 
+def test_forward_staged_and_register_k_agree():
+    # the forward stages K through LDS for key sets of at most 2^17 keys and loads it into
+    # MFMA registers above that; both orders give the same products.  The same 512 queries,
+    # at positions below 2^17, against exactly 2^17 keys and against 256 more that no query
+    # can select (they lie past every query's causal range): ids, O and LSE equal bit for bit
+    Sq, Sk0, H, topk = 512, 1 << 17, 16, 512
+    rng = np.random.default_rng([Sk0, 17])
+    qi, ki, wi = _int_inputs(Sq, Sk0 + 256, seed=17)
+    q = _bits(rng.standard_normal((Sq, H, 128)).astype(np.float32))
+    k = _bits(rng.standard_normal((Sk0 + 256, 128)).astype(np.float32))
+    v = _bits(rng.standard_normal((Sk0 + 256, 128)).astype(np.float32))
+    pos = np.sort(rng.choice(Sk0, size=Sq, replace=False)).astype(np.int32)
+    pos[-8:] = np.arange(Sk0 - 8, Sk0, dtype=np.int32)   # rows that reach the last keys
+    tq = dev_i32(pos)
+    dqi, dwi, dq = dev_bf16(qi), dev_bf16(wi), dev_bf16(q)
+    res = []
+    for Sk in (Sk0, Sk0 + 256):
+        note(f"forward, {Sk} keys ({'K staged' if Sk <= Sk0 else 'K in registers'})")
+        dki, dk, dv = dev_bf16(ki[:Sk]), dev_bf16(k[:Sk]), dev_bf16(v[:Sk])
+        res.append(D.index_attn_fwd(dqi, dki, dwi, dq, dk, dv, topk=topk, q_pos=tq, scale=SCALE))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("idx", "out", "lse"), res[0], res[1]):
+        assert torch.equal(a, b), f"{name} differs between the staged and the register K forward"
+    rows = sample_rows(Sq, topk, pos, n_random=12)
+    ref_idx = O.index_topk(qi, ki[:Sk0], wi, pos, topk, rows=rows)
+    assert_idx_equal("staged-K idx", res[0][0][torch.from_numpy(rows).cuda()].cpu().numpy(), ref_idx, rows)
+    full_idx = np.zeros((Sq, topk), np.int32)
+    full_idx[rows] = ref_idx
+    o_ref, _ = O.sparse_attn_fwd(q, k[:Sk0], v[:Sk0], full_idx, pos, SCALE, rows=rows)
+    assert_close("staged-K O", host_f64(res[0][1][torch.from_numpy(rows).cuda()]), o_ref)
+
+
 def test_s4k_workload_every_row():
     # the S = 4096 workload (H = 4, top-128, its own seeded inputs) through the benchmark's entry
     # point, compared element by element on every row: idx exactly, O and LSE to tolerance
