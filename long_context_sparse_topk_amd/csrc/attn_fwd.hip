@@ -14,9 +14,10 @@
 // contiguous 1 KiB segment of K (and of V).
 //   S^T[key, head] = K[key, :] . Q[head, :]      MFMA 16x16x32, keys as M
 //   O^T[dim, head] += V^T[dim, key] P^T[key, head]
-// The K rows are loaded straight into MFMA A-operand registers; V goes
-// through LDS to be read transposed.  With keys as M and heads as N, each lane
-// owns one head, so the online-softmax rescale is a per-lane scalar.
+// V goes through LDS to be read transposed; the K rows go straight into MFMA
+// A-operand registers, or through LDS as well for key sets the caches hold
+// (kStagedMaxKeys).  With keys as M and heads as N, each lane owns one head,
+// so the online-softmax rescale is a per-lane scalar.
 //
 // Gather lane order: in the MFMA operand order the four lanes of a quad read
 // four different rows, and such a gather stays below ~9.5 TB/s even when
@@ -25,8 +26,9 @@
 // and ~8% more from beyond it (a probe gathering random rows of 0.5 MB to
 // 256 MB tables).  V, which is staged through LDS anyway, is loaded in the
 // row-contiguous order: S = 2^20 141.6 -> 139.4 ms, S = 2^15 3.6 -> 2.6 ms,
-// S = 2^12 0.147 -> 0.105 ms, same outputs.  K read through LDS in that
-// order as well helped less than the extra LDS round trip cost at S = 2^20.
+// S = 2^12 0.147 -> 0.105 ms, same outputs.  K is staged the same way when
+// the key set is small (kStagedMaxKeys below); at S = 2^20 the extra LDS
+// round trip costs more than the row-contiguous order gains.
 
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
